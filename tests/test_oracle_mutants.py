@@ -1,0 +1,73 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Every mutant is a one-line source edit of ``oracle/mzref.py`` (a flipped
+sign, a wrong index, a dropped term, an inverted mask...).  The edited
+module is executed on the CPU and swapped in for the real oracle while the
+pins run; a mutant that passes every pin means the pins have a hole.
+"""
+import inspect
+import types
+
+import pytest
+
+from oracle import mzref
+from tests import oracle_pins
+
+SRC = inspect.getsource(mzref)
+
+MUTANTS = {
+    "rope_sign": ("out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
+    "rope_half_split": ("x0, x1 = x[..., 0::2], x[..., 1::2]", "x0, x1 = x[..., :D // 2], x[..., D // 2:]"),
+    "rope_freq_no_2": ("np.power(float(base), -2.0 * i / head_dim)", "np.power(float(base), -1.0 * i / head_dim)"),
+    "rope_k_unrotated": ("kh = rope_interleaved(kh, pk[b], rope_base)", "kh = kh"),
+    "rope_partial_off_by_one": ("min(pe_attn_head, n_heads_q)", "min(pe_attn_head + 1, n_heads_q)"),
+    "gqa_modulo": ("hk = h // G", "hk = h % Hkv"),
+    "scale_inverted": ("if scale <= 0:\n        scale = 1.0 / math.sqrt(D)\n    n_rot",
+                       "if scale <= 0:\n        scale = math.sqrt(D)\n    n_rot"),
+    "no_max_subtraction": ("m_safe = np.where(any_live, m, 0.0)", "m_safe = np.zeros_like(m)"),
+    "max_over_masked": ("m = np.where(live, s, -np.inf).max(axis=1, initial=-np.inf)",
+                        "m = s.max(axis=1, initial=-np.inf)"),
+    "masked_keys_included": ("p = np.where(live, e, 0.0)", "p = np.where(np.isfinite(e), e, 0.0)"),
+    "no_normalisation": ("(p[any_live] @ v) / l[any_live, None]", "(p[any_live] @ v)"),
+    "lse_drops_max": ("m_safe + np.log(np.where(any_live, l, 1.0))", "np.log(np.where(any_live, l, 1.0))"),
+    "mask_polarity": ("return np.broadcast_to(m, (B, m.shape[1], Sq, Sk))",
+                      "return np.broadcast_to(~m, (B, m.shape[1], Sq, Sk))"),
+    "segment_padding_attends": ("live = (sq[:, :, None] >= 0) & (sq[:, :, None] == sk[:, None, :])",
+                                "live = (sq[:, :, None] == sk[:, None, :])"),
+    "segment_pos_no_restart": ("            start = i\n", "            pass\n"),
+    "decode_span_inclusive": ("in_span = np.arange(C) < span", "in_span = np.arange(C) <= span"),
+    "decode_q_rope_dropped": ("qh = rope_interleaved(qh, np.asarray(q_pos)[b], rope_base)", "qh = qh"),
+    "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "fp16_bias": ("(e - 15)", "(e - 14)"),
+    "fp16_subnormal": ("sub = np.ldexp(f, -24)", "sub = np.ldexp(f, -23)"),
+    "empty_row_nan": ("o = np.zeros((q.shape[0], v.shape[1]))", "o = np.full((q.shape[0], v.shape[1]), np.nan)"),
+}
+
+
+def _mutant_module(old, new):
+    assert SRC.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+    mod = types.ModuleType("mzref_mutant")
+    mod.__dict__["__name__"] = "mzref_mutant"
+    exec(compile(SRC.replace(old, new), "mzref_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    old, new = MUTANTS[name]
+    monkeypatch.setattr(oracle_pins, "mzref", _mutant_module(old, new))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 - any failure detects the mutant
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+            break
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_module_passes(monkeypatch):
+    """The executed copy itself (no edit) passes every pin."""
+    monkeypatch.setattr(oracle_pins, "mzref", _mutant_module("import math\n", "import math\n"))
+    for pin in oracle_pins.ALL_PINS:
+        pin()
