@@ -1,0 +1,211 @@
+/*
+ * mzattn.h - masked bidirectional multi-head attention for AMD Instinct
+ * MI355X (gfx950), C ABI.
+ *
+ * Two operations, both defined by the source pages of three speech engines:
+ *
+ *   mzattn_fwd     softmax(scale * Q K^T restricted to live keys) V with no
+ *                  causal mask.  The live set comes from a 4-D boolean mask
+ *                  (OmniVoice page, "What matches upstream", attention-mask
+ *                  bullet: a full 4-D boolean mask, K/V heads repeated to
+ *                  the query heads) or from segment ids that pack the
+ *                  conditional and unconditional guidance rows side by side
+ *                  under a block-diagonal mask, positions restarting at 0 in
+ *                  each segment (OmniVoice page, "Memory and speed",
+ *                  packed_guidance).  Optional interleaved rotary embedding
+ *                  on all heads or on the first pe_attn_head heads (F5-TTS
+ *                  page, "Variants" table and "How it works").
+ *
+ *   mzattn_decode  one generation step: a few queries against a static KV
+ *                  cache under an explicit boolean mask, over the key span
+ *                  [0, span) (VoxCPM page, "What matches upstream",
+ *                  attention bullet, and "Memory and speed",
+ *                  attention_span).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *   library never allocates, frees or keeps device memory between calls;
+ *   scratch space is the caller's `workspace`.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  Buffers must stay valid until the stream has passed the call.
+ * - Every argument is checked on the host before anything is launched; on
+ *   error nothing is written and a negative status is returned.
+ *   mzattn_last_error() then gives a thread-local detail message.
+ * - Q, K, V and O share one element type (mz_dtype).  Element strides are
+ *   given for the (batch, head, sequence) dims; the head_dim dim is
+ *   contiguous (stride 1).  Base pointers must be 16-byte aligned and every
+ *   stride a multiple of 8 elements (fp16/bf16) or 4 elements (fp32).
+ * - Boolean masks are bytes, nonzero = the key takes part; each of the 4
+ *   mask strides (in bytes) may be 0 to broadcast that dim, the last
+ *   (key) stride must be 1.
+ * - A query with no live key produces an all-zero output row (and
+ *   lse = -inf).  Masked keys contribute exactly nothing: any finite
+ *   values in masked K/V positions leave the output unchanged.  NaN or Inf
+ *   in masked positions is outside the contract.
+ * - Fully masked query rows, empty batches and empty sequences are legal.
+ */
+#ifndef MZATTN_H_
+#define MZATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MZATTN_VERSION 100 /* major * 10000 + minor * 100 + patch */
+
+/* ---- status codes ------------------------------------------------------ */
+#define MZ_OK 0
+#define MZ_ERR_NULL (-1)        /* a required pointer is NULL                 */
+#define MZ_ERR_SHAPE (-2)       /* inconsistent or out-of-range sizes         */
+#define MZ_ERR_DTYPE (-3)       /* unknown element type                       */
+#define MZ_ERR_STRIDE (-4)      /* negative stride, or a stride the kernels
+                                   cannot take (mask key stride != 1)         */
+#define MZ_ERR_ALIGN (-5)       /* base pointer / stride misaligned           */
+#define MZ_ERR_UNSUPPORTED (-6) /* valid request this build does not cover    */
+#define MZ_ERR_WORKSPACE (-7)   /* workspace missing, too small or misaligned */
+#define MZ_ERR_ABI (-8)         /* struct_size does not match this library    */
+#define MZ_ERR_HIP (-9)         /* a HIP launch failed                        */
+#define MZ_ERR_VALUE (-10)      /* bad scalar: scale, rope_base, span ...     */
+
+/* ---- enums ------------------------------------------------------------- */
+typedef enum mz_dtype { MZ_F32 = 0, MZ_F16 = 1, MZ_BF16 = 2 } mz_dtype;
+
+typedef enum mz_mask_kind {
+  MZ_MASK_NONE = 0,    /* every key is live                                  */
+  MZ_MASK_BOOL = 1,    /* live(b,h,i,j) = mask[b,h,i,j] != 0                 */
+  MZ_MASK_SEGMENT = 2  /* live(b,i,j) = seg_q[b,i] >= 0 && seg_q[b,i] == seg_k[b,j] */
+} mz_mask_kind;
+
+/* ---- mzattn_fwd -------------------------------------------------------- */
+/*
+ * Layouts (element strides, d contiguous):
+ *   q [batch, heads_q,  seq_q, head_dim]   o  same shape as q
+ *   k [batch, heads_kv, seq_k, head_dim]   v  same shape as k
+ * GQA: heads_q must be a multiple of heads_kv; query head h reads K/V head
+ * h / (heads_q / heads_kv) (each K/V head repeated G times in a row).
+ * head_dim: 64 or 128.  seq_q, seq_k: 0 .. 2^24.
+ *
+ * scale: <= 0 selects 1/sqrt(head_dim); otherwise used as given.
+ * rope_base: 0 = no rotary embedding; > 0 rotates adjacent pairs
+ *   (x[2i], x[2i+1]) of q and k by pos * rope_base^(-2i/head_dim).
+ * pe_attn_head: < 0 rotates every head; n >= 0 rotates query heads 0..n-1
+ *   and the K heads they read.  With GQA only "none" (0) or "all" (< 0 or
+ *   >= heads_q) is accepted (MZ_ERR_UNSUPPORTED otherwise).
+ * pos_q / pos_k: optional int32 positions [batch, seq] with batch stride
+ *   pos_*_stride_b (0 = shared by all rows).  When NULL: 0..seq-1, or in
+ *   MZ_MASK_SEGMENT mode the index within the token's segment.
+ * mask: bytes, [batch|1, heads_q|1, seq_q|1, seq_k] via mask_stride.
+ * seg_q / seg_k: int32 [batch, seq] segment ids, non-decreasing along each
+ *   row (each id occupies one contiguous run); ids < 0 mark padding, which
+ *   neither attends nor is attended to.  Results for rows that violate the
+ *   ordering are unspecified (memory accesses stay in bounds).
+ * lse: optional fp32 [batch, heads_q, seq_q] (contiguous), natural-log
+ *   log-sum-exp of the scaled live scores; -inf for rows with no live key.
+ * workspace: device scratch of at least mzattn_fwd_workspace_size() bytes,
+ *   256-byte aligned; contents need no initialisation.
+ */
+typedef struct mzattn_fwd_args {
+  uint32_t struct_size; /* = sizeof(mzattn_fwd_args), else MZ_ERR_ABI */
+  int32_t dtype;        /* mz_dtype */
+  int32_t batch, heads_q, heads_kv, seq_q, seq_k, head_dim;
+  int32_t pe_attn_head;
+  int32_t mask_kind;    /* mz_mask_kind */
+  float scale;
+  int32_t reserved0;    /* must be 0 */
+  double rope_base;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3]; /* (b, h, s) */
+  const int32_t* pos_q;
+  const int32_t* pos_k;
+  int64_t pos_q_stride_b, pos_k_stride_b;
+  const uint8_t* mask;
+  int64_t mask_stride[4]; /* bytes, (b, h, i, j); j stride must be 1 */
+  const int32_t* seg_q;
+  const int32_t* seg_k;
+  int64_t seg_q_stride_b, seg_k_stride_b;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} mzattn_fwd_args;
+
+/* Launch the forward on `stream`.  Returns MZ_OK or a negative status. */
+int mzattn_fwd(const mzattn_fwd_args* args, void* stream);
+
+/* Bytes of workspace the call needs (depends on shapes, dtype, mask kind,
+ * RoPE); pointer fields are not read.  Returns MZ_OK or a status. */
+int mzattn_fwd_workspace_size(const mzattn_fwd_args* args, size_t* bytes);
+
+/* Host-only check of every argument; makes no HIP call. */
+int mzattn_validate_fwd(const mzattn_fwd_args* args);
+
+/* ---- mzattn_decode ----------------------------------------------------- */
+/*
+ * Layouts (element strides, d contiguous):
+ *   q        [batch, heads_q,  q_len,     head_dim]   o same shape as q
+ *   k_cache  [batch, heads_kv, cache_len, head_dim]   v_cache same shape
+ * Keys j in [0, span) are considered, span <= cache_len; key j is live for
+ * query t of head h iff j < span and mask[b, h, t, j] != 0 (mask NULL =
+ * every key in the span).  The cache holds keys already rotated; with
+ * rope_base > 0 the queries are rotated at q_pos [batch, q_len] (int32,
+ * batch stride q_pos_stride_b, required then).  q_len: 1 .. 16.
+ * heads_q / heads_kv * q_len must not exceed 64.  head_dim: 64 or 128.
+ *
+ * The result does not depend on span beyond the last live key, bit for
+ * bit: keys are reduced in fixed 128-key chunks aligned to key index 0,
+ * merged in chunk order, and a chunk with no live key is an exact identity.
+ *
+ * workspace: at least mzattn_decode_workspace_size() bytes, 256-byte
+ * aligned.  Its first MZATTN_DECODE_COUNTER_BYTES bytes are arrival
+ * counters that must be zero before the first call with this workspace;
+ * every completed call leaves them zero again.  Calls that share a
+ * workspace must not overlap in time (use one workspace per stream).
+ */
+#define MZATTN_DECODE_CHUNK 128
+#define MZATTN_DECODE_COUNTER_BYTES 4096
+
+typedef struct mzattn_decode_args {
+  uint32_t struct_size; /* = sizeof(mzattn_decode_args), else MZ_ERR_ABI */
+  int32_t dtype;
+  int32_t batch, heads_q, heads_kv, q_len, head_dim, cache_len, span;
+  float scale;
+  double rope_base;
+  const void* q;
+  int64_t q_stride[3];
+  const void* k_cache;
+  int64_t k_stride[3];
+  const void* v_cache;
+  int64_t v_stride[3];
+  void* o;
+  int64_t o_stride[3];
+  const int32_t* q_pos;
+  int64_t q_pos_stride_b;
+  const uint8_t* mask;
+  int64_t mask_stride[4]; /* bytes, (b, h, t, j); j stride must be 1 */
+  void* workspace;
+  size_t workspace_bytes;
+} mzattn_decode_args;
+
+int mzattn_decode(const mzattn_decode_args* args, void* stream);
+int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes);
+int mzattn_validate_decode(const mzattn_decode_args* args);
+
+/* ---- misc -------------------------------------------------------------- */
+/* Static description of a status code. */
+const char* mzattn_strerror(int status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* mzattn_last_error(void);
+/* MZATTN_VERSION of the built library. */
+int mzattn_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MZATTN_H_ */

@@ -1,0 +1,17 @@
+"""Masked bidirectional attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libmzattn.so`` (hand-written HIP, C ABI declared in
+``include/mzattn.h``); this package only marshals torch tensors into it.
+
+    from masked_bidirectional_attention_amd import mzattn_fwd, mzattn_decode
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    MzattnError,
+    MzattnNotBuilt,
+    lib,
+    mzattn_decode,
+    mzattn_fwd,
+)
+
+__all__ = ["mzattn_fwd", "mzattn_decode", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]

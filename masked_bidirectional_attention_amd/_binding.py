@@ -1,0 +1,351 @@
+"""ctypes binding of libmzattn.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module turns torch tensors
+into the C argument structs of ``include/mzattn.h``, allocates outputs and
+workspaces with torch (device memory is torch's), and passes torch's
+current HIP stream.  There is no fallback: if the library is missing,
+every call raises ``MzattnNotBuilt``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmzattn.so")
+
+# status codes (include/mzattn.h)
+MZ_OK = 0
+MZ_ERR_NULL = -1
+MZ_ERR_SHAPE = -2
+MZ_ERR_DTYPE = -3
+MZ_ERR_STRIDE = -4
+MZ_ERR_ALIGN = -5
+MZ_ERR_UNSUPPORTED = -6
+MZ_ERR_WORKSPACE = -7
+MZ_ERR_ABI = -8
+MZ_ERR_HIP = -9
+MZ_ERR_VALUE = -10
+
+MZ_F32, MZ_F16, MZ_BF16 = 0, 1, 2
+MZ_MASK_NONE, MZ_MASK_BOOL, MZ_MASK_SEGMENT = 0, 1, 2
+DECODE_COUNTER_BYTES = 4096
+
+_i64x3 = ctypes.c_int64 * 3
+_i64x4 = ctypes.c_int64 * 4
+
+
+class MzattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mzattn status {status}: {msg}")
+        self.status = status
+
+
+class MzattnNotBuilt(RuntimeError):
+    pass
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("seq_q", ctypes.c_int32),
+        ("seq_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("pe_attn_head", ctypes.c_int32),
+        ("mask_kind", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("reserved0", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("q_stride", _i64x3),
+        ("k_stride", _i64x3),
+        ("v_stride", _i64x3),
+        ("o_stride", _i64x3),
+        ("pos_q", ctypes.c_void_p),
+        ("pos_k", ctypes.c_void_p),
+        ("pos_q_stride_b", ctypes.c_int64),
+        ("pos_k_stride_b", ctypes.c_int64),
+        ("mask", ctypes.c_void_p),
+        ("mask_stride", _i64x4),
+        ("seg_q", ctypes.c_void_p),
+        ("seg_k", ctypes.c_void_p),
+        ("seg_q_stride_b", ctypes.c_int64),
+        ("seg_k_stride_b", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("cache_len", ctypes.c_int32),
+        ("span", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("rope_base", ctypes.c_double),
+        ("q", ctypes.c_void_p),
+        ("q_stride", _i64x3),
+        ("k_cache", ctypes.c_void_p),
+        ("k_stride", _i64x3),
+        ("v_cache", ctypes.c_void_p),
+        ("v_stride", _i64x3),
+        ("o", ctypes.c_void_p),
+        ("o_stride", _i64x3),
+        ("q_pos", ctypes.c_void_p),
+        ("q_pos_stride_b", ctypes.c_int64),
+        ("mask", ctypes.c_void_p),
+        ("mask_stride", _i64x4),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+# exported C symbols and their signatures
+_SIGNATURES = {
+    "mzattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "mzattn_fwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "mzattn_validate_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs)]),
+    "mzattn_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
+    "mzattn_decode_workspace_size": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "mzattn_validate_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs)]),
+    "mzattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "mzattn_last_error": (ctypes.c_char_p, []),
+    "mzattn_version": (ctypes.c_int, []),
+}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise MzattnNotBuilt(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m masked_bidirectional_attention_amd.build`")
+                l = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    fn = getattr(l, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = l
+    return _lib
+
+
+def _check(status: int):
+    if status != MZ_OK:
+        L = lib()
+        detail = L.mzattn_last_error().decode()
+        raise MzattnError(status, f"{L.mzattn_strerror(status).decode()}: {detail}")
+
+
+def new_fwd_args() -> FwdArgs:
+    a = FwdArgs()
+    a.struct_size = ctypes.sizeof(FwdArgs)
+    return a
+
+
+def new_decode_args() -> DecodeArgs:
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    return a
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch  # noqa: WPS433 - torch is only needed for tensors
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: MZ_F32, torch.float16: MZ_F16, torch.bfloat16: MZ_BF16}
+    if t.dtype not in codes:
+        raise MzattnError(MZ_ERR_DTYPE, f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _strides3(t, name):
+    if t.dim() != 4:
+        raise MzattnError(MZ_ERR_SHAPE, f"{name} must be 4-D [B, H, S, D]")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise MzattnError(MZ_ERR_STRIDE, f"{name} head_dim must be contiguous")
+    return _i64x3(*(t.stride(i) if t.shape[i] > 1 else 0 for i in range(3)))
+
+
+def _mask_strides(m, B, H, Sq, Sk, name="mask"):
+    torch = _torch()
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise MzattnError(MZ_ERR_DTYPE, f"{name} must be bool or uint8")
+    if m.dim() != 4:
+        raise MzattnError(MZ_ERR_SHAPE, f"{name} must be 4-D")
+    want = (B, H, Sq, Sk)
+    st = []
+    for i in range(4):
+        if m.shape[i] == want[i] and want[i] != 1:
+            st.append(m.stride(i))
+        elif m.shape[i] == 1:
+            st.append(0 if i < 3 else m.stride(i))
+        else:
+            raise MzattnError(MZ_ERR_SHAPE, f"{name} dim {i} is {m.shape[i]}, expected {want[i]} or 1")
+    if Sk == 1:
+        st[3] = 1
+    return m, _i64x4(*st)
+
+
+class _Workspaces:
+    """Per (device, stream) scratch buffers, grown on demand.  Decode
+    workspaces start zeroed (arrival counters) and the library leaves the
+    counters zero after every call."""
+
+    def __init__(self):
+        self._bufs = {}
+        self._lock = threading.Lock()
+
+    def get(self, kind: str, device, stream_ptr: int, nbytes: int, zero: bool):
+        torch = _torch()
+        key = (kind, device.index, stream_ptr)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                n = max(nbytes, 1 << 20)
+                buf = (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device=device)
+                self._bufs[key] = buf
+            return buf
+
+
+_WS = _Workspaces()
+
+
+def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
+               scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
+               out=None, return_lse: bool = False, workspace=None, stream=None):
+    """Masked bidirectional attention forward (see ``mzattn_fwd`` in
+    include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
+    same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
+    [B, S] (segment mode).  Returns o (and lse when ``return_lse``)."""
+    torch = _torch()
+    L = lib()
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    a = new_fwd_args()
+    a.dtype = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise MzattnError(MZ_ERR_DTYPE, "q, k, v must share one dtype")
+    a.batch, a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim = B, Hq, Hkv, Sq, Sk, D
+    a.pe_attn_head = pe_attn_head
+    a.scale = float(scale)
+    a.rope_base = float(rope_base)
+    o = out if out is not None else torch.empty(B, Hq, Sq, D, dtype=q.dtype, device=q.device)
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
+    a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
+    keep = [q, k, v, o]
+    if mask is not None and seg_q is not None:
+        raise MzattnError(MZ_ERR_UNSUPPORTED, "give either mask or segment ids")
+    if mask is not None:
+        a.mask_kind = MZ_MASK_BOOL
+        m, st = _mask_strides(mask, B, Hq, Sq, Sk)
+        a.mask, a.mask_stride = m.data_ptr(), st
+        keep.append(m)
+    elif seg_q is not None:
+        a.mask_kind = MZ_MASK_SEGMENT
+        seg_k = seg_q if seg_k is None else seg_k
+        for s_ in (seg_q, seg_k):
+            if s_.dtype != torch.int32 or s_.dim() != 2:
+                raise MzattnError(MZ_ERR_DTYPE, "segment ids must be int32 [B, S]")
+        a.seg_q, a.seg_k = seg_q.data_ptr(), seg_k.data_ptr()
+        a.seg_q_stride_b = seg_q.stride(0) if seg_q.shape[0] > 1 else 0
+        a.seg_k_stride_b = seg_k.stride(0) if seg_k.shape[0] > 1 else 0
+        keep += [seg_q, seg_k]
+    for name, pos in (("pos_q", pos_q), ("pos_k", pos_k)):
+        if pos is not None:
+            if pos.dtype != torch.int32 or pos.dim() != 2:
+                raise MzattnError(MZ_ERR_DTYPE, f"{name} must be int32 [B, S]")
+            setattr(a, name, pos.data_ptr())
+            setattr(a, name + "_stride_b", pos.stride(0) if pos.shape[0] > 1 else 0)
+            keep.append(pos)
+    lse = None
+    if return_lse:
+        lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+        a.lse = lse.data_ptr()
+    need = ctypes.c_size_t(0)
+    _check(L.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    if need.value > 0:
+        if workspace is None:
+            workspace = _WS.get("fwd", q.device, s.cuda_stream, need.value, zero=False)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(L.mzattn_fwd(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream)))
+    del keep
+    return (o, lse) if return_lse else o
+
+
+def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
+                  scale: float = 0.0, rope_base: float = 0.0, q_pos=None, out=None,
+                  workspace=None, stream=None):
+    """One static-cache step (see ``mzattn_decode`` in include/mzattn.h).
+    q [B, Hq, q_len, D]; k_cache / v_cache [B, Hkv, cache_len, D]; keys
+    [0, span) considered (default: the whole cache); mask: bool
+    [B|1, Hq|1, q_len|1, cache_len] or None."""
+    torch = _torch()
+    L = lib()
+    B, Hq, T, D = q.shape
+    Hkv, C = k_cache.shape[1], k_cache.shape[2]
+    a = new_decode_args()
+    a.dtype = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise MzattnError(MZ_ERR_DTYPE, "q and the caches must share one dtype")
+    a.batch, a.heads_q, a.heads_kv, a.q_len, a.head_dim, a.cache_len = B, Hq, Hkv, T, D, C
+    a.span = C if span is None else int(span)
+    a.scale = float(scale)
+    a.rope_base = float(rope_base)
+    o = out if out is not None else torch.empty(B, Hq, T, D, dtype=q.dtype, device=q.device)
+    a.q, a.k_cache, a.v_cache, a.o = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr()
+    a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k_cache, "k_cache")
+    a.v_stride, a.o_stride = _strides3(v_cache, "v_cache"), _strides3(o, "o")
+    keep = [q, k_cache, v_cache, o]
+    if mask is not None:
+        m, st = _mask_strides(mask, B, Hq, T, C)
+        a.mask, a.mask_stride = m.data_ptr(), st
+        keep.append(m)
+    if q_pos is not None:
+        if q_pos.dtype != torch.int32 or q_pos.dim() != 2:
+            raise MzattnError(MZ_ERR_DTYPE, "q_pos must be int32 [B, q_len]")
+        a.q_pos = q_pos.data_ptr()
+        a.q_pos_stride_b = q_pos.stride(0) if q_pos.shape[0] > 1 else 0
+        keep.append(q_pos)
+    need = ctypes.c_size_t(0)
+    _check(L.mzattn_decode_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    if workspace is None:
+        workspace = _WS.get("decode", q.device, s.cuda_stream, need.value, zero=True)
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(L.mzattn_decode(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream)))
+    del keep
+    return o

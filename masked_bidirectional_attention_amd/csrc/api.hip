@@ -1,0 +1,419 @@
+// mzattn C ABI: host-side argument checks, workspace carving and dispatch.
+// The checks make no HIP call, so mzattn_validate_* runs on machines
+// without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mzattn.h"
+#include "mz_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MZ_OK;
+}
+
+constexpr int64_t kMaxSeq = int64_t(1) << 20;
+constexpr int kMaxBatch = 65535;
+constexpr int kRopeTableMax = 16384;  // positions held in the cos/sin table
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_size(int dtype) { return dtype == MZ_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// forward plan
+// ---------------------------------------------------------------------------
+struct FwdPlan {
+  bool empty = false;
+  int n_qt = 0, n_kt = 0, bm = 0;
+  int n_rot = 0, n_rot_kv = 0, tab_len = 0;
+  int Bm = 1, Hm = 1;
+  size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_cls = 0;
+  bool need_qpos = false;
+  size_t bytes = 0;
+};
+
+int check_strides3(const int64_t* s, int vec, const char* name) {
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0) return fail(MZ_ERR_STRIDE, "%s_stride[%d] = %lld is negative", name, i, (long long)s[i]);
+    if (s[i] % vec != 0)
+      return fail(MZ_ERR_ALIGN, "%s_stride[%d] = %lld is not a multiple of %d elements", name, i,
+                  (long long)s[i], vec);
+  }
+  return MZ_OK;
+}
+
+// Shape-only part of the forward checks and the workspace plan.
+int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
+  if (a == nullptr) return fail(MZ_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(mzattn_fwd_args))
+    return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_fwd_args) %zu", a->struct_size,
+                sizeof(mzattn_fwd_args));
+  if (a->reserved0 != 0) return fail(MZ_ERR_ABI, "reserved0 must be 0");
+  if (a->dtype != MZ_F32 && a->dtype != MZ_F16 && a->dtype != MZ_BF16)
+    return fail(MZ_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->batch < 0 || a->batch > kMaxBatch) return fail(MZ_ERR_SHAPE, "batch %d outside [0, %d]", a->batch, kMaxBatch);
+  if (a->heads_q < 1 || a->heads_kv < 1 || a->heads_q > 65535 || a->heads_kv > 65535)
+    return fail(MZ_ERR_SHAPE, "heads_q %d / heads_kv %d must be in [1, 65535]", a->heads_q, a->heads_kv);
+  if (a->heads_q % a->heads_kv != 0)
+    return fail(MZ_ERR_SHAPE, "heads_q %d is not a multiple of heads_kv %d", a->heads_q, a->heads_kv);
+  if (a->seq_q < 0 || a->seq_k < 0 || a->seq_q > kMaxSeq || a->seq_k > kMaxSeq)
+    return fail(MZ_ERR_SHAPE, "seq_q %d / seq_k %d outside [0, %lld]", a->seq_q, a->seq_k, (long long)kMaxSeq);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(MZ_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", a->head_dim);
+  if (a->mask_kind != MZ_MASK_NONE && a->mask_kind != MZ_MASK_BOOL && a->mask_kind != MZ_MASK_SEGMENT)
+    return fail(MZ_ERR_UNSUPPORTED, "unknown mask_kind %d", a->mask_kind);
+  if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
+  if (!isfinite(a->rope_base) || a->rope_base < 0.0)
+    return fail(MZ_ERR_VALUE, "rope_base must be finite and >= 0");
+  if (a->rope_base > 0.0 && a->rope_base == 1.0)
+    return fail(MZ_ERR_VALUE, "rope_base 1 gives no frequencies");
+
+  const int Hq = a->heads_q, Hkv = a->heads_kv, G = Hq / Hkv;
+  int n_rot = 0;
+  if (a->rope_base > 0.0) n_rot = a->pe_attn_head < 0 ? Hq : (a->pe_attn_head < Hq ? a->pe_attn_head : Hq);
+  if (G > 1 && n_rot != 0 && n_rot != Hq)
+    return fail(MZ_ERR_UNSUPPORTED, "pe_attn_head %d with GQA (G = %d): only 0 or all heads", a->pe_attn_head, G);
+  pl->n_rot = n_rot;
+  pl->n_rot_kv = G > 1 ? (n_rot ? Hkv : 0) : n_rot;
+
+  pl->bm = a->dtype == MZ_F32 ? mz::F32_BM : mz::FWD_BM;
+  pl->n_qt = (a->seq_q + pl->bm - 1) / pl->bm;
+  pl->n_kt = (a->seq_k + mz::FWD_BN - 1) / mz::FWD_BN;
+  pl->empty = a->batch == 0 || a->seq_q == 0;
+
+  if (a->mask_kind == MZ_MASK_BOOL) {
+    if (a->mask_stride[3] != 1) return fail(MZ_ERR_STRIDE, "mask_stride[3] must be 1 (got %lld)", (long long)a->mask_stride[3]);
+    for (int i = 0; i < 3; ++i)
+      if (a->mask_stride[i] < 0) return fail(MZ_ERR_STRIDE, "mask_stride[%d] is negative", i);
+    pl->Bm = a->mask_stride[0] == 0 ? 1 : a->batch;
+    pl->Hm = a->mask_stride[1] == 0 ? 1 : Hq;
+  }
+  if ((int64_t)a->batch * Hq * pl->n_qt >= (int64_t(1) << 31))
+    return fail(MZ_ERR_SHAPE, "too many query tiles");
+  if (a->mask_kind == MZ_MASK_BOOL && (int64_t)pl->Bm * pl->Hm * pl->n_qt * pl->n_kt >= (int64_t(1) << 31))
+    return fail(MZ_ERR_SHAPE, "too many mask tiles");
+
+  // workspace carve-up
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    const size_t o = align256(off);
+    off = o + bytes;
+    return o;
+  };
+  const int D = a->head_dim;
+  if (n_rot > 0) {
+    int len = a->seq_q > a->seq_k ? a->seq_q : a->seq_k;
+    if (len > kRopeTableMax) len = kRopeTableMax;
+    if (len < 1) len = 1;
+    pl->tab_len = len;
+    pl->off_tab = carve((size_t)len * (D / 2) * sizeof(float) * 2);
+  }
+  if (pl->n_rot_kv > 0) pl->off_krot = carve((size_t)a->batch * pl->n_rot_kv * a->seq_k * D * elem_size(a->dtype));
+  if (a->mask_kind == MZ_MASK_SEGMENT) {
+    pl->off_qrange = carve((size_t)a->batch * a->seq_q * 8);
+    pl->off_qtrange = carve((size_t)a->batch * pl->n_qt * 16);
+    if (n_rot > 0) {
+      pl->need_qpos = true;
+      pl->off_qpos = carve((size_t)a->batch * a->seq_q * 4);
+    }
+  }
+  if (a->mask_kind == MZ_MASK_BOOL) pl->off_cls = carve((size_t)pl->Bm * pl->Hm * pl->n_qt * pl->n_kt);
+  pl->bytes = off == 0 ? 0 : align256(off);
+  return MZ_OK;
+}
+
+int validate_fwd_full(const mzattn_fwd_args* a, FwdPlan* pl) {
+  int st = plan_fwd(a, pl);
+  if (st != MZ_OK) return st;
+  if (pl->empty) return MZ_OK;
+  const int vec = a->dtype == MZ_F32 ? 4 : 8;
+  if (a->q == nullptr || a->o == nullptr) return fail(MZ_ERR_NULL, "q and o must not be NULL");
+  if (a->seq_k > 0 && (a->k == nullptr || a->v == nullptr)) return fail(MZ_ERR_NULL, "k and v must not be NULL");
+  const void* ptrs[4] = {a->q, a->k, a->v, a->o};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(MZ_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  if ((st = check_strides3(a->q_stride, vec, "q")) != MZ_OK) return st;
+  if ((st = check_strides3(a->k_stride, vec, "k")) != MZ_OK) return st;
+  if ((st = check_strides3(a->v_stride, vec, "v")) != MZ_OK) return st;
+  if ((st = check_strides3(a->o_stride, vec, "o")) != MZ_OK) return st;
+  if (a->pos_q_stride_b < 0 || a->pos_k_stride_b < 0) return fail(MZ_ERR_STRIDE, "position strides must be >= 0");
+  if (a->mask_kind == MZ_MASK_BOOL && a->mask == nullptr) return fail(MZ_ERR_NULL, "mask_kind BOOL needs mask");
+  if (a->mask_kind == MZ_MASK_SEGMENT) {
+    if (a->seg_q == nullptr || (a->seg_k == nullptr && a->seq_k > 0))
+      return fail(MZ_ERR_NULL, "mask_kind SEGMENT needs seg_q and seg_k");
+    if (a->seg_q_stride_b < 0 || a->seg_k_stride_b < 0) return fail(MZ_ERR_STRIDE, "segment strides must be >= 0");
+  }
+  if (a->lse && !aligned(a->lse, 4)) return fail(MZ_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (pl->bytes > 0) {
+    if (a->workspace == nullptr) return fail(MZ_ERR_WORKSPACE, "workspace of %zu bytes required", pl->bytes);
+    if (a->workspace_bytes < pl->bytes)
+      return fail(MZ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, pl->bytes);
+    if (!aligned(a->workspace, 256)) return fail(MZ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  return MZ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode plan
+// ---------------------------------------------------------------------------
+struct DecPlan {
+  bool empty = false;
+  int n_chunks = 0, n_chunks_max = 0, R = 0;
+  size_t off_ml = 0, off_acc = 0, off_qrot = 0;
+  size_t bytes = 0;
+};
+
+int plan_decode(const mzattn_decode_args* a, DecPlan* pl) {
+  if (a == nullptr) return fail(MZ_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(mzattn_decode_args))
+    return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_decode_args) %zu", a->struct_size,
+                sizeof(mzattn_decode_args));
+  if (a->dtype != MZ_F32 && a->dtype != MZ_F16 && a->dtype != MZ_BF16)
+    return fail(MZ_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->batch < 0 || a->batch > kMaxBatch) return fail(MZ_ERR_SHAPE, "batch %d outside [0, %d]", a->batch, kMaxBatch);
+  if (a->heads_q < 1 || a->heads_kv < 1 || a->heads_q > 65535 || a->heads_kv > 65535)
+    return fail(MZ_ERR_SHAPE, "heads_q %d / heads_kv %d must be in [1, 65535]", a->heads_q, a->heads_kv);
+  if (a->heads_q % a->heads_kv != 0)
+    return fail(MZ_ERR_SHAPE, "heads_q %d is not a multiple of heads_kv %d", a->heads_q, a->heads_kv);
+  if (a->q_len < 1 || a->q_len > 16) return fail(MZ_ERR_SHAPE, "q_len %d outside [1, 16]", a->q_len);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(MZ_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", a->head_dim);
+  if (a->cache_len < 0 || a->cache_len > (1 << 24)) return fail(MZ_ERR_SHAPE, "cache_len %d outside [0, 2^24]", a->cache_len);
+  if (a->span < 0 || a->span > a->cache_len)
+    return fail(MZ_ERR_VALUE, "span %d outside [0, cache_len %d]", a->span, a->cache_len);
+  const int G = a->heads_q / a->heads_kv;
+  if ((int64_t)G * a->q_len > 64)
+    return fail(MZ_ERR_UNSUPPORTED, "heads_q / heads_kv * q_len = %lld exceeds 64", (long long)G * a->q_len);
+  if ((int64_t)a->batch * a->heads_kv * 4 > MZATTN_DECODE_COUNTER_BYTES)
+    return fail(MZ_ERR_UNSUPPORTED, "batch * heads_kv = %lld exceeds %d", (long long)a->batch * a->heads_kv,
+                MZATTN_DECODE_COUNTER_BYTES / 4);
+  if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
+  if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
+    return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
+  pl->R = G * a->q_len;
+  pl->n_chunks = a->span > 0 ? (a->span + mz::DEC_CHUNK - 1) / mz::DEC_CHUNK : 1;
+  pl->n_chunks_max = a->cache_len > 0 ? (a->cache_len + mz::DEC_CHUNK - 1) / mz::DEC_CHUNK : 1;
+  pl->empty = a->batch == 0;
+  if ((int64_t)a->batch * a->heads_kv * pl->n_chunks >= (int64_t(1) << 31)) return fail(MZ_ERR_SHAPE, "grid too large");
+  size_t off = MZATTN_DECODE_COUNTER_BYTES;
+  auto carve = [&](size_t bytes) {
+    const size_t o = align256(off);
+    off = o + bytes;
+    return o;
+  };
+  const size_t units = (size_t)a->batch * a->heads_kv;
+  pl->off_ml = carve(units * pl->n_chunks_max * pl->R * sizeof(float) * 2);
+  pl->off_acc = carve(units * pl->n_chunks_max * pl->R * a->head_dim * sizeof(float));
+  if (a->rope_base > 0.0)
+    pl->off_qrot = carve((size_t)a->batch * a->heads_q * a->q_len * a->head_dim * elem_size(a->dtype));
+  pl->bytes = align256(off);
+  return MZ_OK;
+}
+
+int validate_decode_full(const mzattn_decode_args* a, DecPlan* pl) {
+  int st = plan_decode(a, pl);
+  if (st != MZ_OK) return st;
+  if (pl->empty) return MZ_OK;
+  const int vec = a->dtype == MZ_F32 ? 4 : 8;
+  if (a->q == nullptr || a->o == nullptr) return fail(MZ_ERR_NULL, "q and o must not be NULL");
+  if (a->cache_len > 0 && (a->k_cache == nullptr || a->v_cache == nullptr))
+    return fail(MZ_ERR_NULL, "k_cache and v_cache must not be NULL");
+  const void* ptrs[4] = {a->q, a->k_cache, a->v_cache, a->o};
+  const char* names[4] = {"q", "k_cache", "v_cache", "o"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && !aligned(ptrs[i], 16)) return fail(MZ_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  if ((st = check_strides3(a->q_stride, vec, "q")) != MZ_OK) return st;
+  if ((st = check_strides3(a->k_stride, vec, "k")) != MZ_OK) return st;
+  if ((st = check_strides3(a->v_stride, vec, "v")) != MZ_OK) return st;
+  if ((st = check_strides3(a->o_stride, vec, "o")) != MZ_OK) return st;
+  if (a->mask) {
+    if (a->mask_stride[3] != 1) return fail(MZ_ERR_STRIDE, "mask_stride[3] must be 1 (got %lld)", (long long)a->mask_stride[3]);
+    for (int i = 0; i < 3; ++i)
+      if (a->mask_stride[i] < 0) return fail(MZ_ERR_STRIDE, "mask_stride[%d] is negative", i);
+  }
+  if (a->rope_base > 0.0) {
+    if (a->q_pos == nullptr) return fail(MZ_ERR_NULL, "rope_base > 0 needs q_pos");
+    if (a->q_pos_stride_b < 0) return fail(MZ_ERR_STRIDE, "q_pos_stride_b must be >= 0");
+  }
+  if (a->workspace == nullptr) return fail(MZ_ERR_WORKSPACE, "workspace of %zu bytes required", pl->bytes);
+  if (a->workspace_bytes < pl->bytes)
+    return fail(MZ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, pl->bytes);
+  if (!aligned(a->workspace, 256)) return fail(MZ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return MZ_OK;
+}
+
+float scale_log2(float scale, int D) {
+  const double s = scale > 0.f ? (double)scale : 1.0 / sqrt((double)D);
+  return (float)(s * 1.4426950408889634074);  // log2(e)
+}
+
+}  // namespace
+
+extern "C" {
+
+int mzattn_version(void) { return MZATTN_VERSION; }
+
+const char* mzattn_strerror(int status) {
+  switch (status) {
+    case MZ_OK: return "ok";
+    case MZ_ERR_NULL: return "a required pointer is NULL";
+    case MZ_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case MZ_ERR_DTYPE: return "unknown element type";
+    case MZ_ERR_STRIDE: return "invalid stride";
+    case MZ_ERR_ALIGN: return "misaligned pointer or stride";
+    case MZ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MZ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MZ_ERR_ABI: return "argument struct does not match this library";
+    case MZ_ERR_HIP: return "HIP launch failed";
+    case MZ_ERR_VALUE: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+const char* mzattn_last_error(void) { return g_last_error.c_str(); }
+
+int mzattn_fwd_workspace_size(const mzattn_fwd_args* args, size_t* bytes) {
+  if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");
+  FwdPlan pl;
+  const int st = plan_fwd(args, &pl);
+  if (st != MZ_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+int mzattn_validate_fwd(const mzattn_fwd_args* args) {
+  FwdPlan pl;
+  const int st = validate_fwd_full(args, &pl);
+  return st == MZ_OK ? ok() : st;
+}
+
+int mzattn_fwd(const mzattn_fwd_args* a, void* stream) {
+  FwdPlan pl;
+  const int st = validate_fwd_full(a, &pl);
+  if (st != MZ_OK) return st;
+  if (pl.empty) return ok();
+  mz::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.dtype = a->dtype;
+  p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.G = a->heads_q / a->heads_kv;
+  p.Sq = a->seq_q; p.Sk = a->seq_k; p.D = a->head_dim;
+  p.n_qt = pl.n_qt; p.n_kt = pl.n_kt;
+  p.mask_kind = a->mask_kind;
+  p.scale_log2 = scale_log2(a->scale, a->head_dim);
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = a->q_stride[i]; p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; p.os[i] = a->o_stride[i];
+  }
+  char* ws = static_cast<char*>(a->workspace);
+  p.n_rot = pl.n_rot; p.n_rot_kv = pl.n_rot_kv;
+  if (pl.n_rot > 0) {
+    p.log2_base = log2(a->rope_base);
+    p.rope_tab = reinterpret_cast<float2*>(ws + pl.off_tab);
+    p.rope_tab_len = pl.tab_len;
+    if (a->pos_q) { p.pos_q_mode = mz::POS_ARRAY; p.pos_q = a->pos_q; p.pos_q_sb = a->pos_q_stride_b; }
+    else if (a->mask_kind == MZ_MASK_SEGMENT) {
+      p.pos_q_mode = mz::POS_SEGMENT; p.pos_q = reinterpret_cast<int32_t*>(ws + pl.off_qpos); p.pos_q_sb = a->seq_q;
+    } else p.pos_q_mode = mz::POS_ARANGE;
+    if (a->pos_k) { p.pos_k_mode = mz::POS_ARRAY; p.pos_k = a->pos_k; p.pos_k_sb = a->pos_k_stride_b; }
+    else p.pos_k_mode = a->mask_kind == MZ_MASK_SEGMENT ? mz::POS_SEGMENT : mz::POS_ARANGE;
+    if (pl.n_rot_kv > 0) p.k_rot = ws + pl.off_krot;
+  }
+  p.Bm = pl.Bm; p.Hm = pl.Hm;
+  if (a->mask_kind == MZ_MASK_BOOL) {
+    p.mask = a->mask;
+    for (int i = 0; i < 4; ++i) p.ms[i] = a->mask_stride[i];
+    p.tile_cls = reinterpret_cast<uint8_t*>(ws + pl.off_cls);
+    p.mask_vec16 = aligned(a->mask, 16) && a->mask_stride[0] % 16 == 0 && a->mask_stride[1] % 16 == 0 &&
+                   a->mask_stride[2] % 16 == 0;
+  }
+  if (a->mask_kind == MZ_MASK_SEGMENT) {
+    p.seg_q = a->seg_q; p.seg_k = a->seg_k;
+    p.seg_q_sb = a->seg_q_stride_b; p.seg_k_sb = a->seg_k_stride_b;
+    p.q_range = reinterpret_cast<int2*>(ws + pl.off_qrange);
+    p.qt_range = reinterpret_cast<int4*>(ws + pl.off_qtrange);
+    p.qpos_ws = (pl.need_qpos && a->pos_q == nullptr) ? reinterpret_cast<int32_t*>(ws + pl.off_qpos) : nullptr;
+  }
+  p.lse = a->lse;
+  const hipError_t e = mz::launch_fwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MZ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes) {
+  if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");
+  DecPlan pl;
+  const int st = plan_decode(args, &pl);
+  if (st != MZ_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+int mzattn_validate_decode(const mzattn_decode_args* args) {
+  DecPlan pl;
+  const int st = validate_decode_full(args, &pl);
+  return st == MZ_OK ? ok() : st;
+}
+
+int mzattn_decode(const mzattn_decode_args* a, void* stream) {
+  DecPlan pl;
+  const int st = validate_decode_full(a, &pl);
+  if (st != MZ_OK) return st;
+  if (pl.empty) return ok();
+  mz::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.dtype = a->dtype;
+  p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.G = a->heads_q / a->heads_kv;
+  p.T = a->q_len; p.R = pl.R; p.C = a->cache_len; p.span = a->span; p.D = a->head_dim;
+  p.n_chunks = pl.n_chunks;
+  p.scale_log2 = scale_log2(a->scale, a->head_dim);
+  char* ws = static_cast<char*>(a->workspace);
+  if (a->rope_base > 0.0) {
+    p.rope = 1;
+    p.log2_base = log2(a->rope_base);
+    p.q_in = a->q;
+    for (int i = 0; i < 3; ++i) p.q_in_s[i] = a->q_stride[i];
+    p.q_pos = a->q_pos; p.q_pos_sb = a->q_pos_stride_b;
+    p.q = ws + pl.off_qrot;
+    p.qs[0] = (int64_t)a->heads_q * a->q_len * a->head_dim;
+    p.qs[1] = (int64_t)a->q_len * a->head_dim;
+    p.qs[2] = a->head_dim;
+  } else {
+    p.q = a->q;
+    for (int i = 0; i < 3; ++i) p.qs[i] = a->q_stride[i];
+  }
+  p.k = a->k_cache; p.v = a->v_cache; p.o = a->o;
+  for (int i = 0; i < 3; ++i) { p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; p.os[i] = a->o_stride[i]; }
+  p.mask = a->mask;
+  if (a->mask)
+    for (int i = 0; i < 4; ++i) p.ms[i] = a->mask_stride[i];
+  p.counters = reinterpret_cast<uint32_t*>(ws);
+  p.part_ml = reinterpret_cast<float2*>(ws + pl.off_ml);
+  p.part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
+  const hipError_t e = mz::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MZ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,388 @@
+// mzattn_decode kernels for gfx950: a few queries against a static KV cache.
+//
+// VoxCPM page, "What matches upstream" (attention bullet) and "Memory and
+// speed" (attention_span): each generation step attends to the cache under
+// an explicit boolean mask; masked positions add exact zeros, so a key span
+// cut anywhere past the last live key must not change the result.
+//
+// Split-K over fixed 128-key chunks aligned to key index 0.  Each
+// work-group reduces one chunk of one (batch, kv-head) for all G*q_len
+// query rows of that head group (the rows share every K/V byte it loads),
+// writes a partial (m, l, acc), and the last work-group to arrive for the
+// (batch, kv-head) folds the partials in chunk order.  A chunk with no live
+// key is skipped by the fold, which is an exact identity, and chunk
+// boundaries do not depend on the span, so any span past the last live key
+// gives the same bits.
+#include "mz_common.h"
+#include "mz_internal.h"
+
+namespace mz {
+
+// ---------------------------------------------------------------------------
+// Optional: rotate q at q_pos into the workspace (every head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void decode_q_rotate16_kernel(const DecodeParams p) {
+  const int half = p.D / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)p.B * p.Hq * p.T * half;
+  if (idx >= n) return;
+  const int i = (int)(idx % half);
+  const int64_t row = idx / half;
+  const int t = (int)(row % p.T);
+  const int h = (int)((row / p.T) % p.Hq);
+  const int b = (int)(row / ((int64_t)p.T * p.Hq));
+  const uint16_t* src = (const uint16_t*)p.q_in + b * p.q_in_s[0] + h * p.q_in_s[1] + (int64_t)t * p.q_in_s[2];
+  const uint32_t w = *(const uint32_t*)(src + 2 * i);
+  const float a = Elem<T>::to_f32((uint16_t)(w & 0xFFFF));
+  const float c = Elem<T>::to_f32((uint16_t)(w >> 16));
+  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
+  ((uint32_t*)p.q)[row * half + i] = Elem<T>::pack2(fmaf(a, cs.x, -c * cs.y), fmaf(c, cs.x, a * cs.y));
+}
+
+__global__ void decode_q_rotate32_kernel(const DecodeParams p) {
+  const int half = p.D / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)p.B * p.Hq * p.T * half;
+  if (idx >= n) return;
+  const int i = (int)(idx % half);
+  const int64_t row = idx / half;
+  const int t = (int)(row % p.T);
+  const int h = (int)((row / p.T) % p.Hq);
+  const int b = (int)(row / ((int64_t)p.T * p.Hq));
+  const float* src = (const float*)p.q_in + b * p.q_in_s[0] + h * p.q_in_s[1] + (int64_t)t * p.q_in_s[2];
+  const float2 x = *(const float2*)(src + 2 * i);
+  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
+  ((float2*)p.q)[row * half + i] = make_float2(fmaf(x.x, cs.x, -x.y * cs.y), fmaf(x.y, cs.x, x.x * cs.y));
+}
+
+__device__ inline bool dec_live(const DecodeParams& p, int b, int kvh, int n, int key) {
+  if (n >= p.R || key >= p.span) return false;
+  if (p.mask == nullptr) return true;
+  const int g = n / p.T, t = n % p.T;
+  const int h = kvh * p.G + g;
+  return p.mask[b * p.ms[0] + h * p.ms[1] + t * p.ms[2] + key] != 0;
+}
+
+// ---------------------------------------------------------------------------
+// Arrival + fixed-order fold of the chunk partials (shared by all dtypes).
+// Returns after the fold on the last work-group; earlier ones return early.
+// ---------------------------------------------------------------------------
+template <typename OutStore>
+__device__ void decode_finish(const DecodeParams& p, int b, int kvh, OutStore store) {
+  __shared__ int s_last;
+  const int unit = b * p.Hkv + kvh;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(&p.counters[unit], 1u);
+    s_last = prev == (unsigned)(p.n_chunks - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int D4 = p.D / 4;
+  for (int item = threadIdx.x; item < p.R * D4; item += blockDim.x) {
+    const int n = item / D4, d = (item % D4) * 4;
+    float m = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float2* ml = p.part_ml + (int64_t)unit * p.n_chunks * p.R + n;
+    const float* pa = p.part_acc + ((int64_t)unit * p.n_chunks * p.R + n) * p.D + d;
+#pragma unroll 4
+    for (int c = 0; c < p.n_chunks; ++c) {
+      const float2 mc = ml[(int64_t)c * p.R];
+      const float4 ac = *(const float4*)(pa + (int64_t)c * p.R * p.D);
+      if (mc.y > 0.f) {
+        const float m_new = fmaxf(m, mc.x);
+        const float sa = fast_exp2(m - m_new);
+        const float sb = fast_exp2(mc.x - m_new);
+        l = l * sa + mc.y * sb;
+        acc.x = acc.x * sa + ac.x * sb;
+        acc.y = acc.y * sa + ac.y * sb;
+        acc.z = acc.z * sa + ac.z * sb;
+        acc.w = acc.w * sa + ac.w * sb;
+        m = m_new;
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int g = n / p.T, t = n % p.T;
+    const int h = kvh * p.G + g;
+    store(b, h, t, d, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+  }
+  if (threadIdx.x == 0) p.counters[unit] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 chunk kernel, MFMA 16x16x32.  Wave w owns keys
+// [chunk*128 + 32w, +32); rows n = g*q_len + t in NB blocks of 16.
+// S^T = K Q^T, then O^T = V^T P^T with V^T read transposed from LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NB>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int NS = D / 32;       // k-steps of K Q^T
+  constexpr int NDB = D / 16;      // 16-row d blocks of O^T
+  constexpr int VSD = D + 16;      // LDS row stride of V (elements)
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;     // V rows per wave load instruction
+  constexpr int NVL = 32 / RPI;    // V loads per lane
+  constexpr int RP = NB * 16;      // padded rows
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[4][32 * VSD];
+  __shared__ float red_m[4][RP];
+  __shared__ float red_l[4][RP];
+  static_assert(sizeof(float) * RP * D <= sizeof(uint16_t) * 4 * 32 * VSD, "acc fold reuses the V region");
+  float* acc_lds = reinterpret_cast<float*>(&Vs[0][0]);
+
+  const int w = blockIdx.x;
+  const int c = w % p.n_chunks;
+  const int unit = w / p.n_chunks;
+  const int kvh = unit % p.Hkv, b = unit / p.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int key0 = c * DEC_CHUNK + wave * 32;
+
+  const uint16_t* kbase = (const uint16_t*)p.k + b * p.ks[0] + kvh * p.ks[1];
+  const uint16_t* vbase = (const uint16_t*)p.v + b * p.vs[0] + kvh * p.vs[1];
+
+  // ---- issue every global load of this wave up front
+  uint4 kf[2][NS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = key0 + kb * 16 + l16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[kb][s] = key < p.span ? *(const uint4*)(kbase + (int64_t)key * p.ks[2] + s * 32 + g4 * 8)
+                               : make_uint4(0, 0, 0, 0);
+  }
+  uint4 vr[NVL];
+#pragma unroll
+  for (int it = 0; it < NVL; ++it) {
+    const int r = it * RPI + lane / CH, cc = lane % CH;
+    const int key = key0 + r;
+    vr[it] = key < p.span ? *(const uint4*)(vbase + (int64_t)key * p.vs[2] + cc * 8) : make_uint4(0, 0, 0, 0);
+  }
+  uint4 qf[NB][NS];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + l16;
+    const int g = n / p.T, t = n % p.T;
+    const int h = kvh * p.G + g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[nb][s] = n < p.R ? *(const uint4*)((const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] +
+                                            (int64_t)t * p.qs[2] + s * 32 + g4 * 8)
+                          : make_uint4(0, 0, 0, 0);
+  }
+  // V rows into this wave's LDS region
+#pragma unroll
+  for (int it = 0; it < NVL; ++it) {
+    const int r = it * RPI + lane / CH, cc = lane % CH;
+    *(uint4*)&Vs[wave][r * VSD + cc * 8] = vr[it];
+  }
+
+  // ---- scores S^T (keys x rows), masked, in the log2 domain
+  f32x4_t sacc[2][NB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) a = mfma16<T>(kf[kb][s], qf[nb][s], a);
+      sacc[kb][nb] = a;
+    }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + l16;
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = key0 + kb * 16 + g4 * 4 + v;
+        const float x = dec_live(p, b, kvh, n, key) ? sacc[kb][nb][v] * p.scale_log2 : -INFINITY;
+        sacc[kb][nb][v] = x;
+        m = fmaxf(m, x);
+      }
+    m = wave_xor_max(m, 16);
+    m = wave_xor_max(m, 32);
+    if (g4 == 0) red_m[wave][n] = m;
+  }
+  __syncthreads();
+  // chunk max over the 4 waves (fixed order), exponentials, partial sums
+  uint4 pb[NB];
+  float m_use[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + l16;
+    const float m = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
+    m_use[nb] = m == -INFINITY ? 0.f : m;
+    float ls = 0.f;
+    uint32_t wv[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float p0 = fast_exp2(sacc[kb][nb][0] - m_use[nb]);
+      const float p1 = fast_exp2(sacc[kb][nb][1] - m_use[nb]);
+      const float p2 = fast_exp2(sacc[kb][nb][2] - m_use[nb]);
+      const float p3 = fast_exp2(sacc[kb][nb][3] - m_use[nb]);
+      ls += (p0 + p1) + (p2 + p3);
+      wv[kb * 2 + 0] = Elem<T>::pack2(p0, p1);
+      wv[kb * 2 + 1] = Elem<T>::pack2(p2, p3);
+    }
+    pb[nb] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (g4 == 0) red_l[wave][n] = ls;
+  }
+
+  // ---- O^T = V^T P^T over this wave's 32 keys
+  f32x4_t oacc[NB][NDB];
+  const int rr = l16 >> 2, cq = l16 & 3;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = db * 16 + 4 * cq;
+    const uint2 a0 = lds_read_tr<T>(&Vs[wave][(g4 * 4 + rr) * VSD + col]);
+    const uint2 a1 = lds_read_tr<T>(&Vs[wave][(16 + g4 * 4 + rr) * VSD + col]);
+    const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      oacc[nb][db] = mfma16<T>(a, pb[nb], z);
+    }
+  }
+  // fold the 4 waves in fixed order through LDS: acc_lds[n][d] (reuses the
+  // V region once every wave has finished reading it)
+  __syncthreads();
+  for (int step = 0; step < 4; ++step) {
+    if (wave == step) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = nb * 16 + l16;
+            const int d = db * 16 + g4 * 4 + v;
+            float* slot = &acc_lds[n * D + d];
+            *slot = step == 0 ? oacc[nb][db][v] : *slot + oacc[nb][db][v];
+          }
+    }
+    __syncthreads();
+  }
+  // ---- write the chunk partial
+  const int64_t pbase = ((int64_t)unit * p.n_chunks + c) * p.R;
+  for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
+    const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
+    *(float4*)(p.part_acc + (pbase + n) * D + d) = *(const float4*)&acc_lds[n * D + d];
+  }
+  for (int n = tid; n < p.R; n += 256) {
+    const float m = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
+    const float l = (red_l[0][n] + red_l[1][n]) + (red_l[2][n] + red_l[3][n]);
+    p.part_ml[pbase + n] = make_float2(m == -INFINITY ? 0.f : m, l);
+  }
+
+  decode_finish(p, b, kvh, [&](int bb, int h, int t, int d, float4 o) {
+    uint16_t* orow = (uint16_t*)p.o + bb * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
+    uint2 st;
+    st.x = Elem<T>::pack2(o.x, o.y);
+    st.y = Elem<T>::pack2(o.z, o.w);
+    *(uint2*)orow = st;
+  });
+}
+
+// ---------------------------------------------------------------------------
+// fp32 chunk kernel: plain FMA, same partial format and fold.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeParams p) {
+  __shared__ float S[64][DEC_CHUNK];
+  __shared__ float s_m[64], s_l[64];
+  const int w = blockIdx.x;
+  const int c = w % p.n_chunks;
+  const int unit = w / p.n_chunks;
+  const int kvh = unit % p.Hkv, b = unit / p.Hkv;
+  const int tid = threadIdx.x;
+  const int D = p.D;
+  const float* kbase = (const float*)p.k + b * p.ks[0] + kvh * p.ks[1];
+  const float* vbase = (const float*)p.v + b * p.vs[0] + kvh * p.vs[1];
+  const int key0 = c * DEC_CHUNK;
+
+  for (int idx = tid; idx < p.R * DEC_CHUNK; idx += 256) {
+    const int n = idx / DEC_CHUNK, j = idx % DEC_CHUNK;
+    const int key = key0 + j;
+    float x = -INFINITY;
+    if (dec_live(p, b, kvh, n, key)) {
+      const int g = n / p.T, t = n % p.T;
+      const int h = kvh * p.G + g;
+      const float* qrow = (const float*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t * p.qs[2];
+      const float* krow = kbase + (int64_t)key * p.ks[2];
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qrow[d], krow[d], acc);
+      x = acc * p.scale_log2;
+    }
+    S[n][j] = x;
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int n = wave; n < p.R; n += 4) {
+    float m = fmaxf(S[n][lane], S[n][lane + 64]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float mu = m == -INFINITY ? 0.f : m;
+    const float p0 = exp2f(S[n][lane] - mu), p1 = exp2f(S[n][lane + 64] - mu);
+    S[n][lane] = p0;
+    S[n][lane + 64] = p1;
+    float l = p0 + p1;
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
+    if (lane == 0) {
+      s_m[n] = mu;
+      s_l[n] = l;
+    }
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)unit * p.n_chunks + c) * p.R;
+  for (int idx = tid; idx < p.R * D; idx += 256) {
+    const int n = idx / D, d = idx % D;
+    float acc = 0.f;
+    for (int j = 0; j < DEC_CHUNK; ++j) {
+      const int key = key0 + j;
+      if (key >= p.span) break;
+      acc = fmaf(S[n][j], vbase[(int64_t)key * p.vs[2] + d], acc);
+    }
+    p.part_acc[(pbase + n) * D + d] = acc;
+  }
+  for (int n = tid; n < p.R; n += 256) p.part_ml[pbase + n] = make_float2(s_m[n], s_l[n]);
+
+  decode_finish(p, b, kvh, [&](int bb, int h, int t, int d, float4 o) {
+    float* orow = (float*)p.o + bb * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
+    *(float4*)orow = o;
+  });
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static void launch_dec16(const DecodeParams& p, unsigned nblk, hipStream_t s) {
+  if (p.R <= 16) decode_mfma_kernel<T, D, 1><<<dim3(nblk), dim3(256), 0, s>>>(p);
+  else if (p.R <= 32) decode_mfma_kernel<T, D, 2><<<dim3(nblk), dim3(256), 0, s>>>(p);
+  else decode_mfma_kernel<T, D, 4><<<dim3(nblk), dim3(256), 0, s>>>(p);
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
+  if (p.rope) {
+    const int64_t n = (int64_t)p.B * p.Hq * p.T * (p.D / 2);
+    const unsigned nb = (unsigned)((n + 255) / 256);
+    if (p.dtype == 0) decode_q_rotate32_kernel<<<dim3(nb), dim3(256), 0, s>>>(p);
+    else if (p.dtype == 2) decode_q_rotate16_kernel<BF16><<<dim3(nb), dim3(256), 0, s>>>(p);
+    else decode_q_rotate16_kernel<F16><<<dim3(nb), dim3(256), 0, s>>>(p);
+  }
+  const unsigned nblk = (unsigned)((int64_t)p.B * p.Hkv * p.n_chunks);
+  if (p.dtype == 0) {
+    decode_f32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
+  } else if (p.dtype == 2) {
+    if (p.D == 64) launch_dec16<BF16, 64>(p, nblk, s);
+    else launch_dec16<BF16, 128>(p, nblk, s);
+  } else {
+    if (p.D == 64) launch_dec16<F16, 64>(p, nblk, s);
+    else launch_dec16<F16, 128>(p, nblk, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mz

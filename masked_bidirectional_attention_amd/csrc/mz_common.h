@@ -1,0 +1,141 @@
+// Device-side helpers shared by the mzattn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mz {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define MZ_LDS __attribute__((address_space(3)))
+
+// Storage tags: the kernels move raw 16-bit patterns and convert explicitly.
+struct BF16 {};
+struct F16 {};
+
+template <typename T> struct Elem;
+template <> struct Elem<BF16> {
+  __device__ static inline float to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+  }
+  // round to nearest even (hardware conversion on gfx950)
+  __device__ static inline uint16_t from_f32(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline uint32_t pack2(float a, float b) {
+    return static_cast<uint32_t>(from_f32(a)) | (static_cast<uint32_t>(from_f32(b)) << 16);
+  }
+};
+template <> struct Elem<F16> {
+  __device__ static inline float to_f32(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+  }
+  __device__ static inline uint16_t from_f32(float x) {
+    _Float16 h = static_cast<_Float16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline uint32_t pack2(float a, float b) {
+    return static_cast<uint32_t>(from_f32(a)) | (static_cast<uint32_t>(from_f32(b)) << 16);
+  }
+};
+
+// ---- MFMA wrappers (operands as raw 16-byte register quads) --------------
+// 32x32x16: A lane l holds A[l%32][(l/32)*8 + e]; B lane l holds
+// B[(l/32)*8 + e][l%32]; C lane l register v holds
+// C[(v/4)*8 + (l/32)*4 + v%4][l%32].
+template <typename T> __device__ inline f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c);
+template <> __device__ inline f32x16_t mfma32<BF16>(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x16_t mfma32<F16>(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+// 16x16x32: A lane l holds A[l%16][(l/16)*8 + e]; B lane l holds
+// B[(l/16)*8 + e][l%16]; C lane l register v holds C[(l/16)*4 + v][l%16].
+template <typename T> __device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c);
+template <> __device__ inline f32x4_t mfma16<BF16>(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x4_t mfma16<F16>(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// ---- LDS transpose read (ds_read_b64_tr_b16) -------------------------------
+// Within each 16-lane group, lane (r = (i/4), c = i%4) supplies the address of
+// 4 consecutive 16-bit elements of "row r"; lane i of the group receives
+// element i%4 of the chunk supplied by lane (r, i/4) for r = 0..3, i.e.
+// column i of the 4 x 16 block formed by the group's rows.
+template <typename T> __device__ inline uint2 lds_read_tr(const uint16_t* p);
+template <> __device__ inline uint2 lds_read_tr<BF16>(const uint16_t* p) {
+  bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MZ_LDS bf16x4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+typedef __fp16 fp16x4_vs_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+template <> __device__ inline uint2 lds_read_tr<F16>(const uint16_t* p) {
+  fp16x4_vs_t r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((MZ_LDS fp16x4_vs_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float wave_xor_max(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+
+// ---- rotary embedding angles -----------------------------------------------
+// Angle of pair i at position p is p * base^(-2i/D), evaluated in fp64 and
+// rounded to fp32 cos / sin at the end.  The table holds positions
+// [0, tab_len); other positions take the same fp64 formula directly, so both
+// routes give identical bits.
+__device__ inline float2 rope_cs_direct(int pos, int i, int D, double log2_base) {
+  double theta = exp2(-(double)(2 * i) / (double)D * log2_base);
+  double ang = (double)pos * theta;
+  double s, c;
+  sincos(ang, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
+__device__ inline float2 rope_cs(const float2* tab, int tab_len, int pos, int i, int D,
+                                 double log2_base) {
+  if (pos >= 0 && pos < tab_len) return tab[(size_t)pos * (D / 2) + i];
+  return rope_cs_direct(pos, i, D, log2_base);
+}
+
+// Rotate the 8 consecutive elements held in a quad (d0 even) in fp32 and
+// round back to the storage type.
+template <typename T>
+__device__ inline uint4 rope_quad(uint4 x, const float2* tab, int tab_len, int pos, int d0, int D,
+                                  double log2_base) {
+  uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float a = Elem<T>::to_f32((uint16_t)(w[t] & 0xFFFF));
+    float b = Elem<T>::to_f32((uint16_t)(w[t] >> 16));
+    float2 cs = rope_cs(tab, tab_len, pos, d0 / 2 + t, D, log2_base);
+    float ra = fmaf(a, cs.x, -b * cs.y);
+    float rb = fmaf(b, cs.x, a * cs.y);
+    w[t] = Elem<T>::pack2(ra, rb);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Map a hardware block id to a work item so that consecutive work items land
+// on one XCD (blocks are dispatched round-robin over the 8 XCDs).
+__device__ inline int xcd_remap(int bid, int n) {
+  const int n8 = n - (n & 7);
+  if (bid >= n8) return bid;
+  return (bid & 7) * (n8 >> 3) + (bid >> 3);
+}
+
+}  // namespace mz

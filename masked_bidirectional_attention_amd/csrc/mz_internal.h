@@ -1,0 +1,88 @@
+// Host <-> kernel plumbing for mzattn: parameter blocks and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mz {
+
+// Tile sizes of the forward: queries per work-group, keys per iteration.
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+// fp32 forward: queries per work-group, keys per LDS tile.
+constexpr int F32_BM = 64;
+constexpr int F32_BN = 32;
+// Decode: keys per chunk (fixed, aligned to key index 0).
+constexpr int DEC_CHUNK = 128;
+
+enum PosMode { POS_ARANGE = 0, POS_ARRAY = 1, POS_SEGMENT = 2 };
+
+struct FwdParams {
+  int dtype, B, Hq, Hkv, G, Sq, Sk, D;
+  int n_qt, n_kt;  // query tiles (FWD_BM or F32_BM), key tiles (FWD_BN)
+  int mask_kind;
+  float scale_log2;  // scale * log2(e)
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  // rotary embedding
+  int n_rot, n_rot_kv;
+  double log2_base;
+  int pos_q_mode, pos_k_mode;
+  const int32_t* pos_q;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
+  int64_t pos_q_sb;
+  const int32_t* pos_k;  // user array (POS_ARRAY); segment-derived on the fly
+  int64_t pos_k_sb;
+  float2* rope_tab;
+  int rope_tab_len;
+  void* k_rot;  // [B][n_rot_kv][Sk][D], storage dtype
+  // boolean mask
+  const uint8_t* mask;
+  int64_t ms[4];
+  int Bm, Hm;
+  int mask_vec16;
+  uint8_t* tile_cls;  // [Bm][Hm][n_qt][n_kt]
+  // segments
+  const int32_t* seg_q;
+  const int32_t* seg_k;
+  int64_t seg_q_sb, seg_k_sb;
+  int2* q_range;   // [B][Sq] live key range of each query
+  int4* qt_range;  // [B][n_qt] (first tile, end tile, first full tile, end full tile)
+  int32_t* qpos_ws;  // [B][Sq] derived query positions
+  float* lse;
+};
+
+struct DecodeParams {
+  int dtype, B, Hq, Hkv, G, T, R, C, span, D;
+  int n_chunks;
+  float scale_log2;
+  const void* q;  // possibly the rotated copy in the workspace
+  int64_t qs[3];
+  const void* k;
+  int64_t ks[3];
+  const void* v;
+  int64_t vs[3];
+  void* o;
+  int64_t os[3];
+  const uint8_t* mask;  // may be NULL
+  int64_t ms[4];
+  // rotary embedding of q (pre-kernel)
+  const void* q_in;
+  int64_t q_in_s[3];
+  const int32_t* q_pos;
+  int64_t q_pos_sb;
+  double log2_base;
+  int rope;
+  // workspace
+  uint32_t* counters;  // [B][Hkv]
+  float2* part_ml;     // [B][Hkv][n_chunks][R]   (m in log2 units, l)
+  float* part_acc;     // [B][Hkv][n_chunks][R][D]
+};
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+
+}  // namespace mz

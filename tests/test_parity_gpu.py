@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 max |d| <= 1e-5; fp16 / bf16 relative L2 <= 4e-3 and
+max |d| <= 2e-2 * max |ref| (checked by ``mzref.within_tolerance``).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from masked_bidirectional_attention_amd import workloads as W
+from oracle import mzref
+from tests.gpu_helpers import (assert_parity, bits, dev, oracle_decode, oracle_fwd, run_decode,
+                               run_fwd, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# the five named workloads at their full sizes
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("materialized", [False, True])
+def test_tiny_cfg_fp32(materialized):
+    case = W.tiny_cfg(materialized)
+    o, lse = run_fwd(case, return_lse=True)
+    ref, lse_ref = oracle_fwd(case)
+    assert_parity("f32", o, ref, case.name)
+    np.testing.assert_allclose(to64(lse), lse_ref, atol=1e-5)
+
+
+def test_f5_dit_layer_fp16():
+    case = W.f5_dit_layer()
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity("f16", o, ref, case.name)
+
+
+def test_qwen_padded_bf16():
+    case = W.qwen_cfg_padded()
+    o, lse = run_fwd(case, return_lse=True)
+    ref, lse_ref = oracle_fwd(case)
+    assert_parity("bf16", o, ref, case.name)
+    # padded query rows of row 1 have no live key: exactly zero, lse -inf
+    assert torch.all(o[1, :, W.QWEN_UNCOND:] == 0)
+    assert torch.all(torch.isinf(lse[1, :, W.QWEN_UNCOND:]))
+    fin = np.isfinite(lse_ref)
+    np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=2e-2)
+
+
+@pytest.mark.parametrize("as_bool", [False, True])
+def test_qwen_packed_bf16(as_bool):
+    padded = W.qwen_cfg_padded()
+    case = W.qwen_cfg_packed(as_bool_mask=as_bool, padded=padded)
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity("bf16", o, ref, case.name)
+
+
+def test_packed_equals_separate_rows():
+    """OmniVoice page, 'Memory and speed': the packed row computes what the
+    two padded rows compute, segment by segment."""
+    padded = W.qwen_cfg_padded()
+    packed = W.qwen_cfg_packed(padded=padded)
+    op = run_fwd(packed)
+    o2 = run_fwd(padded)
+    S, U = W.QWEN_S, W.QWEN_UNCOND
+    a = torch.cat([o2[0:1], o2[1:2, :, :U]], dim=2)
+    st = mzref.parity_stats(to64(op), to64(a))
+    print(f"[packed vs padded] max_abs={st['max_abs']:.3e} rel_l2={st['rel_l2']:.3e} "
+          f"bitwise={torch.equal(op, a)}", flush=True)
+    assert mzref.within_tolerance("bf16", st)
+
+
+@pytest.mark.parametrize("filled", W.VOX_FILLED)
+def test_vox_decode(filled):
+    full = W.vox_decode(filled)
+    o_full = run_decode(full)
+    ref = oracle_decode(full)
+    assert_parity("bf16", o_full, ref, f"{full.name} span=8192")
+    span = W.ceil256(filled)
+    o_cut = run_decode(full, span=span)
+    assert_parity("bf16", o_cut, ref, f"{full.name} span={span}")
+    # the cut past the last live key changes no bit
+    assert np.array_equal(bits(o_full), bits(o_cut)), "span truncation changed bits"
+
+
+# --------------------------------------------------------------------------
+# random shapes: ragged tails, several tiles, GQA, dtypes, mask kinds
+# --------------------------------------------------------------------------
+
+FWD_SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, D
+    (1, 2, 1, 1, 1, 64),
+    (2, 2, 2, 7, 9, 128),
+    (1, 4, 2, 63, 65, 64),
+    (2, 8, 1, 129, 300, 128),
+    (1, 2, 2, 300, 129, 64),
+    (1, 16, 2, 257, 513, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", FWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["none", "bool_full", "bool_key", "bool_blocky", "segment"])
+def test_random_fwd(dtype, shape, kind):
+    B, Hq, Hkv, Sq, Sk, D = shape
+    seed = zlib.crc32(repr((dtype, shape, kind)).encode()) % 10000
+    if kind == "segment":
+        if Sq != Sk:
+            pytest.skip("segment mode here packs self-attention rows")
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_SEGMENT, rope_base=1e4, n_segments=3)
+    elif kind == "none":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_NONE, rope_base=1e4)
+    else:
+        mshape = {"bool_full": "full", "bool_key": "key", "bool_blocky": "blocky"}[kind]
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_BOOL, mask_shape=mshape,
+                            rope_base=1e6 if Hq != Hkv else 1e4,
+                            pe_attn_head=-1 if Hq != Hkv else 1)
+    o, lse = run_fwd(case, return_lse=True)
+    ref, lse_ref = oracle_fwd(case)
+    assert_parity(dtype, o, ref, f"{case.name} {shape}")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(to64(lse)), fin)
+    np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=1e-4 if dtype == "f32" else 3e-2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_explicit_positions(dtype):
+    case = W.random_fwd(11, 2, 4, 4, 100, 140, 64, dtype, W.MASK_NONE, rope_base=1e4, explicit_pos=True)
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity(dtype, o, ref, "explicit positions")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, q_len, cache, D, filled, span
+    (1, 2, 1, 1, 64, 64, 64, 64),
+    (2, 16, 2, 1, 1000, 128, 700, 768),
+    (1, 8, 8, 3, 300, 64, 1, 300),
+    (2, 4, 1, 16, 513, 128, 513, 513),
+    (1, 32, 2, 4, 2048, 128, 1500, 1536),
+    (1, 4, 4, 2, 256, 128, 100, 0),
+], ids=lambda s: "x".join(map(str, s)))
+def test_random_decode(dtype, shape):
+    B, Hq, Hkv, T, C, D, filled, span = shape
+    case = W.random_decode(zlib.crc32(repr((dtype, shape)).encode()) % 10000, B, Hq, Hkv, T, C, D, dtype, filled, span,
+                           mask_heads=True, rope_base=1e4 if T > 1 else 0.0)
+    o = run_decode(case)
+    ref = oracle_decode(case)
+    assert_parity(dtype, o, ref, f"decode {shape}")
+
+
+# --------------------------------------------------------------------------
+# invariants and edge cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_single_live_key_is_exact(dtype):
+    """One live key: p = 1, l = 1, so the output is v_j bit for bit."""
+    case = W.random_fwd(21, 1, 2, 2, 70, 90, 64, dtype, W.MASK_BOOL, mask_shape="full")
+    m = torch.zeros(1, 2, 70, 90, dtype=torch.bool)
+    js = torch.randint(0, 90, (2, 70), generator=torch.Generator().manual_seed(3))
+    for h in range(2):
+        m[0, h, torch.arange(70), js[h]] = True
+    case.mask = m
+    o = run_fwd(case).cpu()
+    for h in range(2):
+        assert torch.equal(o[0, h], case.v[0, h, js[h]]), f"head {h}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_garbage_bitwise(dtype):
+    """Finite junk in masked K/V positions leaves the output bit-identical."""
+    case = W.random_fwd(22, 2, 4, 2, 150, 200, 128, dtype, W.MASK_BOOL, mask_shape="key")
+    case.mask[:, :, :, 150:] = False
+    o1 = run_fwd(case)
+    k2, v2 = case.k.clone(), case.v.clone()
+    g = torch.Generator().manual_seed(5)
+    k2[:, :, 150:] = (torch.randn(k2[:, :, 150:].shape, generator=g) * 1000).to(k2.dtype)
+    v2[:, :, 150:] = (torch.randn(v2[:, :, 150:].shape, generator=g) * 1000).to(v2.dtype)
+    o2 = run_fwd(case, k=dev(k2), v=dev(v2))
+    assert torch.equal(o1, o2)
+
+
+def test_decode_masked_garbage_bitwise():
+    case = W.random_decode(23, 2, 16, 2, 1, 1024, 128, "bf16", 300, 1024, garbage=1000.0)
+    clean = W.random_decode(23, 2, 16, 2, 1, 1024, 128, "bf16", 300, 1024)
+    assert torch.equal(run_decode(case), run_decode(clean))
+
+
+def test_fully_masked_and_empty():
+    case = W.random_fwd(24, 1, 2, 2, 40, 50, 64, "bf16", W.MASK_BOOL, mask_shape="full")
+    case.mask[:, :, 5:9] = False
+    o, lse = run_fwd(case, return_lse=True)
+    assert torch.all(o[:, :, 5:9] == 0) and torch.all(torch.isinf(lse[:, :, 5:9]))
+    # no keys at all
+    e = W.random_fwd(25, 1, 2, 2, 10, 0, 64, "bf16")
+    oe = run_fwd(e)
+    assert oe.shape == (1, 2, 10, 64) and torch.all(oe == 0)
+    # no queries: a legal no-op
+    z = W.random_fwd(26, 1, 2, 2, 0, 10, 64, "bf16")
+    assert run_fwd(z).shape == (1, 2, 0, 64)
+
+
+def test_deterministic():
+    case = W.random_fwd(27, 2, 8, 2, 333, 333, 128, "bf16", W.MASK_SEGMENT, rope_base=1e6, n_segments=3)
+    a = run_fwd(case)
+    b = run_fwd(case)
+    assert torch.equal(a, b)
+    d = W.vox_decode(3100)
+    assert torch.equal(run_decode(d), run_decode(d))
+
+
+def test_gqa_equals_repeated_heads():
+    case = W.random_fwd(28, 1, 8, 2, 200, 200, 128, "bf16", W.MASK_BOOL, mask_shape="bcast_h", rope_base=1e6)
+    a = run_fwd(case)
+    rep = W.FwdCase(case.name, case.dtype, case.q, case.k.repeat_interleave(4, 1),
+                    case.v.repeat_interleave(4, 1), rope_base=case.rope_base, mask_kind=case.mask_kind,
+                    mask=case.mask)
+    b = run_fwd(rep)
+    assert torch.equal(a, b)
+
+
+def test_decode_matches_fwd_single_query():
+    """A decode step with q_len 1 equals the forward with Sq = 1 over the
+    same keys (two different kernels; tolerance, not bits)."""
+    d = W.random_decode(29, 2, 8, 2, 1, 600, 128, "bf16", 600, 600, mask_heads=True)
+    od = run_decode(d)
+    f = W.FwdCase("fwd1", "bf16", d.q, d.k_cache, d.v_cache, mask_kind=W.MASK_BOOL, mask=d.mask)
+    of = run_fwd(f)
+    st = mzref.parity_stats(to64(od), to64(of))
+    assert mzref.within_tolerance("bf16", st), st
