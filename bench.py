@@ -1,0 +1,215 @@
+"""Benchmark of the masked-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one pass of the hot path over one batch of synthetic input:
+  1. mzattn_fwd on the packed-guidance workload: one row of 2848 tokens
+     ([2048 conditional | 800 unconditional] segments, block-diagonal,
+     positions restarting at 0), Hq 16 / Hkv 8, head_dim 128, bf16, RoPE
+     base 1e6 on every head -- split into its plan (prepasses) and execute
+     (the attention kernel) launches;
+  2. mzattn_decode on the static-cache step: batch 2, one query, Hq 16 /
+     Hkv 2, head_dim 128, 8192-position cache fully filled (L = 8192), bf16,
+     full span, reading one of 32 rotating cache copies so the step sees
+     cold HBM (537 MB > the 256 MB Infinity Cache).
+
+Inputs are resident in HBM before timing starts.  Prints one JSON line:
+``value`` is the attention kernel's live TFLOP/s on the packed workload
+(the headline), ``decode`` holds the static-cache step's HBM GB/s, each
+with its roofline against MI355X's published peaks, and ``cpu_baseline``
+is the fp64 oracle timed on the host for one full packed-workload call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "masked-attn TFLOP/s & % MFMA peak; static-cache decode HBM GB/s & % peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def live_pairs_packed():
+    from masked_bidirectional_attention_amd import workloads as W
+    return 16 * (W.QWEN_S ** 2 + W.QWEN_UNCOND ** 2)
+
+
+def fwd_flops():
+    """4 * D per live (query, key) pair: 2 for Q.K^T and 2 for P.V."""
+    return 4 * 128 * live_pairs_packed()
+
+
+def decode_bytes(L=8192, span=8192):
+    """K and V rows of the live keys (B 2 x Hkv 2 x L x D 128 x 2 bytes x 2),
+    the mask bytes in the span (2 rows), q and o (2 x 16 x 128 x 2 each)."""
+    return 2 * 2 * L * 128 * 2 * 2 + 2 * span + 2 * (2 * 16 * 128 * 2)
+
+
+def cpu_baseline():
+    import threadpoolctl
+    from masked_bidirectional_attention_amd import workloads as W
+    from oracle import mzref
+
+    c = W.qwen_cfg_packed()
+    bq, bk, bv = W.to_bits(c.q), W.to_bits(c.k), W.to_bits(c.v)
+    seg = c.seg_q.numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:  # repeat the call until about 10 s of host work
+        mzref.mzref_fwd(c.dtype, bq, bk, bv, rope_base=c.rope_base, mask_kind="segment", seg_q=seg, seg_k=seg)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 50:
+            break
+    threads = 0
+    for info in threadpoolctl.threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    return {
+        "value": fwd_flops() * reps / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{reps} full packed-guidance forwards (16 heads, 2848 tokens, {fwd_flops() / 1e9:.2f} "
+                  f"live GFLOP each) through the fp64 numpy oracle: {dt:.2f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cache-copies", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic per launch (from rocprofv3 --pmc), if present")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import masked_bidirectional_attention_amd as mz
+    from masked_bidirectional_attention_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- inputs resident in HBM
+    c3 = W.qwen_cfg_packed()
+    fq, fk, fv = c3.q.to(dev), c3.k.to(dev), c3.v.to(dev)
+    seg = c3.seg_q.to(dev)
+    fwd = mz.FwdCall(fq, fk, fv, seg_q=seg, seg_k=seg, rope_base=c3.rope_base)
+
+    c4 = W.vox_decode(8192)
+    dq, dmask = c4.q.to(dev), c4.mask.to(dev)
+    kc0, vc0 = c4.k_cache.to(dev), c4.v_cache.to(dev)
+    copies = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(max(0, a.cache_copies - 1))]
+    dout = torch.empty_like(dq)
+    torch.cuda.synchronize()
+    print(f"[bench] device {props.name}, {props.multi_processor_count} CUs; inputs resident", file=sys.stderr, flush=True)
+
+    def step(i, evs=None):
+        fwd.plan()
+        if evs:
+            evs[0].record()
+        fwd.execute()
+        if evs:
+            evs[1].record()
+        kc, vc = copies[i % len(copies)]
+        mz.mzattn_decode(dq, kc, vc, span=8192, mask=dmask, scale=c4.scale, out=dout)
+        if evs:
+            evs[2].record()
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {a.warmup} steps done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
+    print(f"[bench] timed {a.steps} steps: {wall / a.steps * 1e3:.3f} ms/step, attention kernel "
+          f"{fwd_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    tflops = fwd_flops() / (fwd_ms * 1e-3) / 1e12
+    gbs = decode_bytes() / (dec_ms * 1e-3) / 1e9
+    traffic = {}
+    if os.path.exists(a.traffic):
+        with open(a.traffic) as f:
+            traffic = json.load(f)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "packed-guidance bidirectional attention: 1 row x 2848 tokens "
+                        "[2048 cond | 800 uncond] block-diagonal, Hq 16 / Hkv 8, D 128, RoPE base 1e6",
+            "decode_workload": "static-cache step: B 2, 1 query, Hq 16 / Hkv 2, D 128, "
+                               "cache 8192 filled 8192, full span, 32 rotating cache copies (cold HBM)",
+            "global_batch": 1,
+            "seq_len": 2848,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "fwd_mfma_kernel<bf16,128>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic.get("fwd_mfma_kernel"),
+            "kernel_us": round(fwd_ms * 1e3, 2),
+            "algorithmic_gflop": round(fwd_flops() / 1e9, 3),
+        },
+        "decode": {
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "roofline": {
+                "kernel": "decode_mfma_kernel<bf16,128,1>",
+                "bound": "hbm",
+                "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic.get("decode_mfma_kernel"),
+                "kernel_us": round(dec_ms * 1e3, 2),
+                "algorithmic_mb": round(decode_bytes() / 1e6, 3),
+            },
+        },
+        "device": props.name,
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

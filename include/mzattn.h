@@ -87,7 +87,7 @@ typedef enum mz_mask_kind {
  *   k [batch, heads_kv, seq_k, head_dim]   v  same shape as k
  * GQA: heads_q must be a multiple of heads_kv; query head h reads K/V head
  * h / (heads_q / heads_kv) (each K/V head repeated G times in a row).
- * head_dim: 64 or 128.  seq_q, seq_k: 0 .. 2^24.
+ * head_dim: 64 or 128.  seq_q, seq_k: 0 .. 2^20.
  *
  * scale: <= 0 selects 1/sqrt(head_dim); otherwise used as given.
  * rope_base: 0 = no rotary embedding; > 0 rotates adjacent pairs
@@ -135,8 +135,21 @@ typedef struct mzattn_fwd_args {
   size_t workspace_bytes;
 } mzattn_fwd_args;
 
-/* Launch the forward on `stream`.  Returns MZ_OK or a negative status. */
+/* Launch the forward on `stream`.  Returns MZ_OK or a negative status.
+ * Equivalent to mzattn_fwd_plan followed by mzattn_fwd_execute. */
 int mzattn_fwd(const mzattn_fwd_args* args, void* stream);
+
+/* The two halves of mzattn_fwd, for callers that time or schedule them
+ * separately.  mzattn_fwd_plan launches the prepasses, which write the
+ * workspace from the mask or segment ids, the positions and K (RoPE table,
+ * rotated K, per-tile key ranges / tile classes).  mzattn_fwd_execute
+ * launches only the attention kernel and reads that workspace: it must
+ * follow a plan with the same arguments, on the same stream (or after it
+ * completed), with the workspace, mask, segment ids, positions and K
+ * unchanged in between.  Same argument checks and status codes as
+ * mzattn_fwd. */
+int mzattn_fwd_plan(const mzattn_fwd_args* args, void* stream);
+int mzattn_fwd_execute(const mzattn_fwd_args* args, void* stream);
 
 /* Bytes of workspace the call needs (depends on shapes, dtype, mask kind,
  * RoPE); pointer fields are not read.  Returns MZ_OK or a status. */

@@ -119,6 +119,8 @@ class DecodeArgs(ctypes.Structure):
 # exported C symbols and their signatures
 _SIGNATURES = {
     "mzattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "mzattn_fwd_plan": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "mzattn_fwd_execute": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "mzattn_fwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "mzattn_validate_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs)]),
     "mzattn_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
@@ -242,6 +244,84 @@ class _Workspaces:
 _WS = _Workspaces()
 
 
+class FwdCall:
+    """A marshalled forward call: the C argument struct plus the tensors it
+    points to (kept alive here).  ``plan()`` / ``execute()`` launch the two
+    halves on the call's stream; ``__call__`` launches both."""
+
+    def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
+                 scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
+                 out=None, return_lse: bool = False, workspace=None, stream=None):
+        torch = _torch()
+        L = lib()
+        B, Hq, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+        a = new_fwd_args()
+        a.dtype = _dtype_code(q)
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise MzattnError(MZ_ERR_DTYPE, "q, k, v must share one dtype")
+        a.batch, a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim = B, Hq, Hkv, Sq, Sk, D
+        a.pe_attn_head = pe_attn_head
+        a.scale = float(scale)
+        a.rope_base = float(rope_base)
+        o = out if out is not None else torch.empty(B, Hq, Sq, D, dtype=q.dtype, device=q.device)
+        a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+        a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
+        a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
+        keep = [q, k, v, o]
+        if mask is not None and seg_q is not None:
+            raise MzattnError(MZ_ERR_UNSUPPORTED, "give either mask or segment ids")
+        if mask is not None:
+            a.mask_kind = MZ_MASK_BOOL
+            m, st = _mask_strides(mask, B, Hq, Sq, Sk)
+            a.mask, a.mask_stride = m.data_ptr(), st
+            keep.append(m)
+        elif seg_q is not None:
+            a.mask_kind = MZ_MASK_SEGMENT
+            seg_k = seg_q if seg_k is None else seg_k
+            for s_ in (seg_q, seg_k):
+                if s_.dtype != torch.int32 or s_.dim() != 2:
+                    raise MzattnError(MZ_ERR_DTYPE, "segment ids must be int32 [B, S]")
+            a.seg_q, a.seg_k = seg_q.data_ptr(), seg_k.data_ptr()
+            a.seg_q_stride_b = seg_q.stride(0) if seg_q.shape[0] > 1 else 0
+            a.seg_k_stride_b = seg_k.stride(0) if seg_k.shape[0] > 1 else 0
+            keep += [seg_q, seg_k]
+        for name, pos in (("pos_q", pos_q), ("pos_k", pos_k)):
+            if pos is not None:
+                if pos.dtype != torch.int32 or pos.dim() != 2:
+                    raise MzattnError(MZ_ERR_DTYPE, f"{name} must be int32 [B, S]")
+                setattr(a, name, pos.data_ptr())
+                setattr(a, name + "_stride_b", pos.stride(0) if pos.shape[0] > 1 else 0)
+                keep.append(pos)
+        self.lse = None
+        if return_lse:
+            self.lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+            a.lse = self.lse.data_ptr()
+        need = ctypes.c_size_t(0)
+        _check(L.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        self.stream = torch.cuda.current_stream(q.device) if stream is None else stream
+        if need.value > 0:
+            if workspace is None:
+                workspace = _WS.get("fwd", q.device, self.stream.cuda_stream, need.value, zero=False)
+            a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+            keep.append(workspace)
+        self.args, self.out, self._keep, self._lib = a, o, keep, L
+        self.workspace_bytes = need.value
+
+    def _launch(self, fn):
+        _check(fn(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
+
+    def plan(self):
+        self._launch(self._lib.mzattn_fwd_plan)
+
+    def execute(self):
+        self._launch(self._lib.mzattn_fwd_execute)
+
+    def __call__(self):
+        self._launch(self._lib.mzattn_fwd)
+        return (self.out, self.lse) if self.lse is not None else self.out
+
+
 def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                out=None, return_lse: bool = False, workspace=None, stream=None):
@@ -249,61 +329,9 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
     same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
     [B, S] (segment mode).  Returns o (and lse when ``return_lse``)."""
-    torch = _torch()
-    L = lib()
-    B, Hq, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
-    a = new_fwd_args()
-    a.dtype = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise MzattnError(MZ_ERR_DTYPE, "q, k, v must share one dtype")
-    a.batch, a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim = B, Hq, Hkv, Sq, Sk, D
-    a.pe_attn_head = pe_attn_head
-    a.scale = float(scale)
-    a.rope_base = float(rope_base)
-    o = out if out is not None else torch.empty(B, Hq, Sq, D, dtype=q.dtype, device=q.device)
-    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
-    a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
-    a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
-    keep = [q, k, v, o]
-    if mask is not None and seg_q is not None:
-        raise MzattnError(MZ_ERR_UNSUPPORTED, "give either mask or segment ids")
-    if mask is not None:
-        a.mask_kind = MZ_MASK_BOOL
-        m, st = _mask_strides(mask, B, Hq, Sq, Sk)
-        a.mask, a.mask_stride = m.data_ptr(), st
-        keep.append(m)
-    elif seg_q is not None:
-        a.mask_kind = MZ_MASK_SEGMENT
-        seg_k = seg_q if seg_k is None else seg_k
-        for s_ in (seg_q, seg_k):
-            if s_.dtype != torch.int32 or s_.dim() != 2:
-                raise MzattnError(MZ_ERR_DTYPE, "segment ids must be int32 [B, S]")
-        a.seg_q, a.seg_k = seg_q.data_ptr(), seg_k.data_ptr()
-        a.seg_q_stride_b = seg_q.stride(0) if seg_q.shape[0] > 1 else 0
-        a.seg_k_stride_b = seg_k.stride(0) if seg_k.shape[0] > 1 else 0
-        keep += [seg_q, seg_k]
-    for name, pos in (("pos_q", pos_q), ("pos_k", pos_k)):
-        if pos is not None:
-            if pos.dtype != torch.int32 or pos.dim() != 2:
-                raise MzattnError(MZ_ERR_DTYPE, f"{name} must be int32 [B, S]")
-            setattr(a, name, pos.data_ptr())
-            setattr(a, name + "_stride_b", pos.stride(0) if pos.shape[0] > 1 else 0)
-            keep.append(pos)
-    lse = None
-    if return_lse:
-        lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
-        a.lse = lse.data_ptr()
-    need = ctypes.c_size_t(0)
-    _check(L.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
-    s = torch.cuda.current_stream(q.device) if stream is None else stream
-    if need.value > 0:
-        if workspace is None:
-            workspace = _WS.get("fwd", q.device, s.cuda_stream, need.value, zero=False)
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(L.mzattn_fwd(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream)))
-    del keep
-    return (o, lse) if return_lse else o
+    return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, pos_q=pos_q, pos_k=pos_k,
+                   scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, out=out,
+                   return_lse=return_lse, workspace=workspace, stream=stream)()
 
 
 def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,

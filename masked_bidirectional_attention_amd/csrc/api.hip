@@ -269,52 +269,8 @@ float scale_log2(float scale, int D) {
   return (float)(s * 1.4426950408889634074);  // log2(e)
 }
 
-}  // namespace
-
-extern "C" {
-
-int mzattn_version(void) { return MZATTN_VERSION; }
-
-const char* mzattn_strerror(int status) {
-  switch (status) {
-    case MZ_OK: return "ok";
-    case MZ_ERR_NULL: return "a required pointer is NULL";
-    case MZ_ERR_SHAPE: return "inconsistent or out-of-range sizes";
-    case MZ_ERR_DTYPE: return "unknown element type";
-    case MZ_ERR_STRIDE: return "invalid stride";
-    case MZ_ERR_ALIGN: return "misaligned pointer or stride";
-    case MZ_ERR_UNSUPPORTED: return "unsupported configuration";
-    case MZ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
-    case MZ_ERR_ABI: return "argument struct does not match this library";
-    case MZ_ERR_HIP: return "HIP launch failed";
-    case MZ_ERR_VALUE: return "invalid scalar argument";
-    default: return "unknown status";
-  }
-}
-
-const char* mzattn_last_error(void) { return g_last_error.c_str(); }
-
-int mzattn_fwd_workspace_size(const mzattn_fwd_args* args, size_t* bytes) {
-  if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");
-  FwdPlan pl;
-  const int st = plan_fwd(args, &pl);
-  if (st != MZ_OK) return st;
-  *bytes = pl.bytes;
-  return ok();
-}
-
-int mzattn_validate_fwd(const mzattn_fwd_args* args) {
-  FwdPlan pl;
-  const int st = validate_fwd_full(args, &pl);
-  return st == MZ_OK ? ok() : st;
-}
-
-int mzattn_fwd(const mzattn_fwd_args* a, void* stream) {
-  FwdPlan pl;
-  const int st = validate_fwd_full(a, &pl);
-  if (st != MZ_OK) return st;
-  if (pl.empty) return ok();
-  mz::FwdParams p;
+// Fill the kernel parameter block of a validated call.
+void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams& p) {
   memset(&p, 0, sizeof(p));
   p.dtype = a->dtype;
   p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.G = a->heads_q / a->heads_kv;
@@ -356,10 +312,71 @@ int mzattn_fwd(const mzattn_fwd_args* a, void* stream) {
     p.qpos_ws = (pl.need_qpos && a->pos_q == nullptr) ? reinterpret_cast<int32_t*>(ws + pl.off_qpos) : nullptr;
   }
   p.lse = a->lse;
-  const hipError_t e = mz::launch_fwd(p, static_cast<hipStream_t>(stream));
+}
+
+enum { FWD_PLAN = 1, FWD_MAIN = 2 };
+
+int run_fwd(const mzattn_fwd_args* a, void* stream, int parts) {
+  FwdPlan pl;
+  const int st = validate_fwd_full(a, &pl);
+  if (st != MZ_OK) return st;
+  if (pl.empty) return ok();
+  mz::FwdParams p;
+  fill_fwd_params(a, pl, p);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (parts & FWD_PLAN) e = mz::launch_fwd_plan(p, s);
+  if (e == hipSuccess && (parts & FWD_MAIN)) e = mz::launch_fwd_main(p, s);
   if (e != hipSuccess) return fail(MZ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+
+}  // namespace
+
+extern "C" {
+
+int mzattn_version(void) { return MZATTN_VERSION; }
+
+const char* mzattn_strerror(int status) {
+  switch (status) {
+    case MZ_OK: return "ok";
+    case MZ_ERR_NULL: return "a required pointer is NULL";
+    case MZ_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case MZ_ERR_DTYPE: return "unknown element type";
+    case MZ_ERR_STRIDE: return "invalid stride";
+    case MZ_ERR_ALIGN: return "misaligned pointer or stride";
+    case MZ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MZ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MZ_ERR_ABI: return "argument struct does not match this library";
+    case MZ_ERR_HIP: return "HIP launch failed";
+    case MZ_ERR_VALUE: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+const char* mzattn_last_error(void) { return g_last_error.c_str(); }
+
+int mzattn_fwd_workspace_size(const mzattn_fwd_args* args, size_t* bytes) {
+  if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");
+  FwdPlan pl;
+  const int st = plan_fwd(args, &pl);
+  if (st != MZ_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+int mzattn_validate_fwd(const mzattn_fwd_args* args) {
+  FwdPlan pl;
+  const int st = validate_fwd_full(args, &pl);
+  return st == MZ_OK ? ok() : st;
+}
+
+int mzattn_fwd(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_PLAN | FWD_MAIN); }
+
+int mzattn_fwd_plan(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_PLAN); }
+
+int mzattn_fwd_execute(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_MAIN); }
 
 int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes) {
   if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");

@@ -551,7 +551,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
+hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
   const bool f32 = p.dtype == 0;
   const int bm = f32 ? F32_BM : FWD_BM;
   if (p.n_rot > 0 && p.rope_tab_len > 0) {
@@ -572,6 +572,11 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
     const int64_t ntiles = (int64_t)p.Bm * p.Hm * p.n_qt * p.n_kt;
     mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
+  const bool f32 = p.dtype == 0;
   const unsigned nwork = (unsigned)((int64_t)p.B * p.Hq * p.n_qt);
   if (f32) {
     if (p.D == 64) fwd_f32_kernel<64><<<dim3(nwork), dim3(64), 0, s>>>(p);

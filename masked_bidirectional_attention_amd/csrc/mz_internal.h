@@ -82,7 +82,8 @@ struct DecodeParams {
   float* part_acc;     // [B][Hkv][n_chunks][R][D]
 };
 
-hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 }  // namespace mz
