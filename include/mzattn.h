@@ -36,6 +36,8 @@
  *   given for the (batch, head, sequence) dims; the head_dim dim is
  *   contiguous (stride 1).  Base pointers must be 16-byte aligned and every
  *   stride a multiple of 8 elements (fp16/bf16) or 4 elements (fp32).
+ *   mzattn_fwd also needs the K and V sequence strides below 2^24 elements
+ *   (MZ_ERR_UNSUPPORTED otherwise).
  * - Boolean masks are bytes, nonzero = the key takes part; each of the 4
  *   mask strides (in bytes) may be 0 to broadcast that dim, the last
  *   (key) stride must be 1.
@@ -172,16 +174,16 @@ int mzattn_validate_fwd(const mzattn_fwd_args* args);
  *
  * The result does not depend on span beyond the last live key, bit for
  * bit: keys are reduced in fixed 128-key chunks aligned to key index 0,
- * merged in chunk order, and a chunk with no live key is an exact identity.
+ * the chunk partials are folded in an order fixed by chunk index, and a
+ * chunk with no live key is an exact identity.
  *
  * workspace: at least mzattn_decode_workspace_size() bytes, 256-byte
- * aligned.  Its first MZATTN_DECODE_COUNTER_BYTES bytes are arrival
- * counters that must be zero before the first call with this workspace;
- * every completed call leaves them zero again.  Calls that share a
- * workspace must not overlap in time (use one workspace per stream).
+ * aligned; contents need no initialisation.  It holds the per-chunk
+ * partials; calls sharing a workspace must not overlap in time (use one
+ * workspace per stream).  Its size depends on cache_len, not on span, so
+ * one workspace serves every step of a generation.
  */
 #define MZATTN_DECODE_CHUNK 128
-#define MZATTN_DECODE_COUNTER_BYTES 4096
 
 typedef struct mzattn_decode_args {
   uint32_t struct_size; /* = sizeof(mzattn_decode_args), else MZ_ERR_ABI */

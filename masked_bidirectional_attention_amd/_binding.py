@@ -31,7 +31,6 @@ MZ_ERR_VALUE = -10
 
 MZ_F32, MZ_F16, MZ_BF16 = 0, 1, 2
 MZ_MASK_NONE, MZ_MASK_BOOL, MZ_MASK_SEGMENT = 0, 1, 2
-DECODE_COUNTER_BYTES = 4096
 
 _i64x3 = ctypes.c_int64 * 3
 _i64x4 = ctypes.c_int64 * 4
@@ -221,9 +220,8 @@ def _mask_strides(m, B, H, Sq, Sk, name="mask"):
 
 
 class _Workspaces:
-    """Per (device, stream) scratch buffers, grown on demand.  Decode
-    workspaces start zeroed (arrival counters) and the library leaves the
-    counters zero after every call."""
+    """Per (device, stream) scratch buffers, grown on demand (contents need
+    no initialisation)."""
 
     def __init__(self):
         self._bufs = {}
@@ -372,7 +370,7 @@ def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
     _check(L.mzattn_decode_workspace_size(ctypes.byref(a), ctypes.byref(need)))
     s = torch.cuda.current_stream(q.device) if stream is None else stream
     if workspace is None:
-        workspace = _WS.get("decode", q.device, s.cuda_stream, need.value, zero=True)
+        workspace = _WS.get("decode", q.device, s.cuda_stream, need.value, zero=False)
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(L.mzattn_decode(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream)))
     del keep

@@ -8,7 +8,7 @@
 
 #include <string>
 
-#include "../../include/mzattn.h"
+#include "mzattn.h"
 #include "mz_internal.h"
 
 namespace {
@@ -48,7 +48,7 @@ struct FwdPlan {
   int n_qt = 0, n_kt = 0, bm = 0;
   int n_rot = 0, n_rot_kv = 0, tab_len = 0;
   int Bm = 1, Hm = 1;
-  size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_cls = 0;
+  size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_kpos = 0, off_cls = 0;
   bool need_qpos = false;
   size_t bytes = 0;
 };
@@ -136,6 +136,7 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
     if (n_rot > 0) {
       pl->need_qpos = true;
       pl->off_qpos = carve((size_t)a->batch * a->seq_q * 4);
+      pl->off_kpos = carve((size_t)a->batch * a->seq_k * 4);
     }
   }
   if (a->mask_kind == MZ_MASK_BOOL) pl->off_cls = carve((size_t)pl->Bm * pl->Hm * pl->n_qt * pl->n_kt);
@@ -158,6 +159,8 @@ int validate_fwd_full(const mzattn_fwd_args* a, FwdPlan* pl) {
   if ((st = check_strides3(a->k_stride, vec, "k")) != MZ_OK) return st;
   if ((st = check_strides3(a->v_stride, vec, "v")) != MZ_OK) return st;
   if ((st = check_strides3(a->o_stride, vec, "o")) != MZ_OK) return st;
+  if (a->k_stride[2] >= (int64_t(1) << 24) || a->v_stride[2] >= (int64_t(1) << 24))
+    return fail(MZ_ERR_UNSUPPORTED, "k / v row strides must be below 2^24 elements");
   if (a->pos_q_stride_b < 0 || a->pos_k_stride_b < 0) return fail(MZ_ERR_STRIDE, "position strides must be >= 0");
   if (a->mask_kind == MZ_MASK_BOOL && a->mask == nullptr) return fail(MZ_ERR_NULL, "mask_kind BOOL needs mask");
   if (a->mask_kind == MZ_MASK_SEGMENT) {
@@ -206,9 +209,6 @@ int plan_decode(const mzattn_decode_args* a, DecPlan* pl) {
   const int G = a->heads_q / a->heads_kv;
   if ((int64_t)G * a->q_len > 64)
     return fail(MZ_ERR_UNSUPPORTED, "heads_q / heads_kv * q_len = %lld exceeds 64", (long long)G * a->q_len);
-  if ((int64_t)a->batch * a->heads_kv * 4 > MZATTN_DECODE_COUNTER_BYTES)
-    return fail(MZ_ERR_UNSUPPORTED, "batch * heads_kv = %lld exceeds %d", (long long)a->batch * a->heads_kv,
-                MZATTN_DECODE_COUNTER_BYTES / 4);
   if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
   if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
     return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
@@ -217,7 +217,7 @@ int plan_decode(const mzattn_decode_args* a, DecPlan* pl) {
   pl->n_chunks_max = a->cache_len > 0 ? (a->cache_len + mz::DEC_CHUNK - 1) / mz::DEC_CHUNK : 1;
   pl->empty = a->batch == 0;
   if ((int64_t)a->batch * a->heads_kv * pl->n_chunks >= (int64_t(1) << 31)) return fail(MZ_ERR_SHAPE, "grid too large");
-  size_t off = MZATTN_DECODE_COUNTER_BYTES;
+  size_t off = 0;
   auto carve = [&](size_t bytes) {
     const size_t o = align256(off);
     off = o + bytes;
@@ -293,7 +293,9 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
       p.pos_q_mode = mz::POS_SEGMENT; p.pos_q = reinterpret_cast<int32_t*>(ws + pl.off_qpos); p.pos_q_sb = a->seq_q;
     } else p.pos_q_mode = mz::POS_ARANGE;
     if (a->pos_k) { p.pos_k_mode = mz::POS_ARRAY; p.pos_k = a->pos_k; p.pos_k_sb = a->pos_k_stride_b; }
-    else p.pos_k_mode = a->mask_kind == MZ_MASK_SEGMENT ? mz::POS_SEGMENT : mz::POS_ARANGE;
+    else if (a->mask_kind == MZ_MASK_SEGMENT) {
+      p.pos_k_mode = mz::POS_SEGMENT; p.pos_k = reinterpret_cast<int32_t*>(ws + pl.off_kpos); p.pos_k_sb = a->seq_k;
+    } else p.pos_k_mode = mz::POS_ARANGE;
     if (pl.n_rot_kv > 0) p.k_rot = ws + pl.off_krot;
   }
   p.Bm = pl.Bm; p.Hm = pl.Hm;
@@ -310,6 +312,7 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
     p.q_range = reinterpret_cast<int2*>(ws + pl.off_qrange);
     p.qt_range = reinterpret_cast<int4*>(ws + pl.off_qtrange);
     p.qpos_ws = (pl.need_qpos && a->pos_q == nullptr) ? reinterpret_cast<int32_t*>(ws + pl.off_qpos) : nullptr;
+    p.kpos_ws = (pl.need_qpos && a->pos_k == nullptr) ? reinterpret_cast<int32_t*>(ws + pl.off_kpos) : nullptr;
   }
   p.lse = a->lse;
 }
@@ -425,7 +428,6 @@ int mzattn_decode(const mzattn_decode_args* a, void* stream) {
   p.mask = a->mask;
   if (a->mask)
     for (int i = 0; i < 4; ++i) p.ms[i] = a->mask_stride[i];
-  p.counters = reinterpret_cast<uint32_t*>(ws);
   p.part_ml = reinterpret_cast<float2*>(ws + pl.off_ml);
   p.part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
   const hipError_t e = mz::launch_decode(p, static_cast<hipStream_t>(stream));

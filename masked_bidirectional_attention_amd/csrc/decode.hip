@@ -6,13 +6,13 @@
 // cut anywhere past the last live key must not change the result.
 //
 // Split-K over fixed 128-key chunks aligned to key index 0.  Each
-// work-group reduces one chunk of one (batch, kv-head) for all G*q_len
-// query rows of that head group (the rows share every K/V byte it loads),
-// writes a partial (m, l, acc), and the last work-group to arrive for the
-// (batch, kv-head) folds the partials in chunk order.  A chunk with no live
-// key is skipped by the fold, which is an exact identity, and chunk
-// boundaries do not depend on the span, so any span past the last live key
-// gives the same bits.
+// work-group of the chunk kernel reduces one chunk of one (batch, kv-head)
+// for all G*q_len query rows of that head group (the rows share every K/V
+// byte it loads) and writes a partial (m, l, acc).  The merge kernel then
+// folds the partials of every row in an order fixed by chunk index alone.
+// A chunk with no live key is skipped by the fold, which is an exact
+// identity, and chunk boundaries do not depend on the span, so any span
+// past the last live key gives the same bits.
 #include "mz_common.h"
 #include "mz_internal.h"
 
@@ -65,51 +65,99 @@ __device__ inline bool dec_live(const DecodeParams& p, int b, int kvh, int n, in
 }
 
 // ---------------------------------------------------------------------------
-// Arrival + fixed-order fold of the chunk partials (shared by all dtypes).
-// Returns after the fold on the last work-group; earlier ones return early.
+// Fold of two partials (m in log2 units, l, acc).  A partial with l == 0 is
+// the identity and is skipped, so folding it changes no bit.
 // ---------------------------------------------------------------------------
-template <typename OutStore>
-__device__ void decode_finish(const DecodeParams& p, int b, int kvh, OutStore store) {
-  __shared__ int s_last;
-  const int unit = b * p.Hkv + kvh;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&p.counters[unit], 1u);
-    s_last = prev == (unsigned)(p.n_chunks - 1);
+struct Part2 {
+  float m, l, a0, a1;
+};
+
+__device__ inline void fold_into(Part2& x, float m, float l, float a0, float a1) {
+  if (!(l > 0.f)) return;
+  if (!(x.l > 0.f)) {
+    x.m = m; x.l = l; x.a0 = a0; x.a1 = a1;
+    return;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int D4 = p.D / 4;
-  for (int item = threadIdx.x; item < p.R * D4; item += blockDim.x) {
-    const int n = item / D4, d = (item % D4) * 4;
-    float m = -INFINITY, l = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float2* ml = p.part_ml + (int64_t)unit * p.n_chunks * p.R + n;
-    const float* pa = p.part_acc + ((int64_t)unit * p.n_chunks * p.R + n) * p.D + d;
-#pragma unroll 4
-    for (int c = 0; c < p.n_chunks; ++c) {
-      const float2 mc = ml[(int64_t)c * p.R];
-      const float4 ac = *(const float4*)(pa + (int64_t)c * p.R * p.D);
-      if (mc.y > 0.f) {
-        const float m_new = fmaxf(m, mc.x);
-        const float sa = fast_exp2(m - m_new);
-        const float sb = fast_exp2(mc.x - m_new);
-        l = l * sa + mc.y * sb;
-        acc.x = acc.x * sa + ac.x * sb;
-        acc.y = acc.y * sa + ac.y * sb;
-        acc.z = acc.z * sa + ac.z * sb;
-        acc.w = acc.w * sa + ac.w * sb;
-        m = m_new;
+  const float mn = fmaxf(x.m, m);
+  const float sa = fast_exp2(x.m - mn), sb = fast_exp2(m - mn);
+  x.l = x.l * sa + l * sb;
+  x.a0 = x.a0 * sa + a0 * sb;
+  x.a1 = x.a1 * sa + a1 * sb;
+  x.m = mn;
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one work-group per (batch, kv-head, row).  The fold order
+// is fixed by chunk index alone: chunks are taken in super-groups of 64;
+// within one, group g of threads folds chunks [g*CG, (g+1)*CG) in order,
+// then the group partials are folded in g order, then super-groups in
+// order.  Chunks at or past n_chunks are identities, so the result does
+// not depend on how many chunks the span covered beyond its live keys.
+// ---------------------------------------------------------------------------
+template <int D, typename Store>
+__device__ void decode_merge_row(const DecodeParams& p, Store store) {
+  constexpr int HD = D / 2;     // d pairs
+  constexpr int NG = 256 / HD;  // chunk groups (4 for D 128, 8 for D 64)
+  constexpr int CG = 64 / NG;   // chunks per group per super-group
+  __shared__ Part2 red[256];
+  const int row = blockIdx.x;  // (unit, n)
+  const int n = row % p.R, unit = row / p.R;
+  const int kvh = unit % p.Hkv, b = unit / p.Hkv;
+  const int t = threadIdx.x, dp = t % HD, g = t / HD;
+  const float2* ml = p.part_ml + (int64_t)unit * p.n_chunks * p.R + n;
+  const float* pa = p.part_acc + ((int64_t)unit * p.n_chunks * p.R + n) * D + 2 * dp;
+  Part2 tot = {0.f, 0.f, 0.f, 0.f};
+  for (int sg = 0; sg * 64 < p.n_chunks; ++sg) {
+    const int c0 = sg * 64 + g * CG;
+    // every load of the group first, then the fold
+    float2 mc[CG], ac[CG];
+#pragma unroll
+    for (int i = 0; i < CG; ++i) {
+      const int c = c0 + i;
+      mc[i] = make_float2(0.f, 0.f);
+      ac[i] = make_float2(0.f, 0.f);
+      if (c < p.n_chunks) {
+        mc[i] = ml[(int64_t)c * p.R];
+        ac[i] = *(const float2*)(pa + (int64_t)c * p.R * D);
       }
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int g = n / p.T, t = n % p.T;
-    const int h = kvh * p.G + g;
-    store(b, h, t, d, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+    Part2 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CG; ++i) fold_into(x, mc[i].x, mc[i].y, ac[i].x, ac[i].y);
+    red[t] = x;
+    __syncthreads();
+    if (g == 0) {
+      Part2 y = red[dp];
+#pragma unroll
+      for (int gg = 1; gg < NG; ++gg) {
+        const Part2 z = red[gg * HD + dp];
+        fold_into(y, z.m, z.l, z.a0, z.a1);
+      }
+      fold_into(tot, y.m, y.l, y.a0, y.a1);
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) p.counters[unit] = 0u;
+  if (g == 0) {
+    const float inv = tot.l > 0.f ? 1.f / tot.l : 0.f;
+    const int gq = n / p.T, tq = n % p.T;
+    store(b, kvh * p.G + gq, tq, 2 * dp, tot.a0 * inv, tot.a1 * inv);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_merge16_kernel(const DecodeParams p) {
+  decode_merge_row<D>(p, [&](int b, int h, int t, int d, float x0, float x1) {
+    uint16_t* orow = (uint16_t*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
+    *(uint32_t*)orow = Elem<T>::pack2(x0, x1);
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge32_kernel(const DecodeParams p) {
+  decode_merge_row<D>(p, [&](int b, int h, int t, int d, float x0, float x1) {
+    float* orow = (float*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
+    *(float2*)orow = make_float2(x0, x1);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -172,6 +220,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
                                             (int64_t)t * p.qs[2] + s * 32 + g4 * 8)
                           : make_uint4(0, 0, 0, 0);
   }
+  // liveness of this lane's score elements (mask loads overlap the K/V loads)
+  bool live[2][NB][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        live[kb][nb][v] = dec_live(p, b, kvh, nb * 16 + l16, key0 + kb * 16 + g4 * 4 + v);
   // V rows into this wave's LDS region
 #pragma unroll
   for (int it = 0; it < NVL; ++it) {
@@ -198,8 +255,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int key = key0 + kb * 16 + g4 * 4 + v;
-        const float x = dec_live(p, b, kvh, n, key) ? sacc[kb][nb][v] * p.scale_log2 : -INFINITY;
+        const float x = live[kb][nb][v] ? sacc[kb][nb][v] * p.scale_log2 : -INFINITY;
         sacc[kb][nb][v] = x;
         m = fmaxf(m, x);
       }
@@ -279,14 +335,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     const float l = (red_l[0][n] + red_l[1][n]) + (red_l[2][n] + red_l[3][n]);
     p.part_ml[pbase + n] = make_float2(m == -INFINITY ? 0.f : m, l);
   }
-
-  decode_finish(p, b, kvh, [&](int bb, int h, int t, int d, float4 o) {
-    uint16_t* orow = (uint16_t*)p.o + bb * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
-    uint2 st;
-    st.x = Elem<T>::pack2(o.x, o.y);
-    st.y = Elem<T>::pack2(o.z, o.w);
-    *(uint2*)orow = st;
-  });
 }
 
 // ---------------------------------------------------------------------------
@@ -349,11 +397,6 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeParams p) {
     p.part_acc[(pbase + n) * D + d] = acc;
   }
   for (int n = tid; n < p.R; n += 256) p.part_ml[pbase + n] = make_float2(s_m[n], s_l[n]);
-
-  decode_finish(p, b, kvh, [&](int bb, int h, int t, int d, float4 o) {
-    float* orow = (float*)p.o + bb * p.os[0] + h * p.os[1] + (int64_t)t * p.os[2] + d;
-    *(float4*)orow = o;
-  });
 }
 
 // ---------------------------------------------------------------------------
@@ -373,14 +416,27 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
     else decode_q_rotate16_kernel<F16><<<dim3(nb), dim3(256), 0, s>>>(p);
   }
   const unsigned nblk = (unsigned)((int64_t)p.B * p.Hkv * p.n_chunks);
+  const unsigned nrows = (unsigned)((int64_t)p.B * p.Hkv * p.R);
   if (p.dtype == 0) {
     decode_f32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
+    if (p.D == 64) decode_merge32_kernel<64><<<dim3(nrows), dim3(256), 0, s>>>(p);
+    else decode_merge32_kernel<128><<<dim3(nrows), dim3(256), 0, s>>>(p);
   } else if (p.dtype == 2) {
-    if (p.D == 64) launch_dec16<BF16, 64>(p, nblk, s);
-    else launch_dec16<BF16, 128>(p, nblk, s);
+    if (p.D == 64) {
+      launch_dec16<BF16, 64>(p, nblk, s);
+      decode_merge16_kernel<BF16, 64><<<dim3(nrows), dim3(256), 0, s>>>(p);
+    } else {
+      launch_dec16<BF16, 128>(p, nblk, s);
+      decode_merge16_kernel<BF16, 128><<<dim3(nrows), dim3(256), 0, s>>>(p);
+    }
   } else {
-    if (p.D == 64) launch_dec16<F16, 64>(p, nblk, s);
-    else launch_dec16<F16, 128>(p, nblk, s);
+    if (p.D == 64) {
+      launch_dec16<F16, 64>(p, nblk, s);
+      decode_merge16_kernel<F16, 64><<<dim3(nrows), dim3(256), 0, s>>>(p);
+    } else {
+      launch_dec16<F16, 128>(p, nblk, s);
+      decode_merge16_kernel<F16, 128><<<dim3(nrows), dim3(256), 0, s>>>(p);
+    }
   }
   return hipGetLastError();
 }

@@ -29,41 +29,72 @@ __global__ void rope_table_kernel(float2* tab, int len, int D, double log2_base)
 // Segment ids are non-decreasing along a row, so the keys sharing a query's
 // id form one contiguous run, found by binary search.
 // ---------------------------------------------------------------------------
-__device__ inline int lower_bound_i32(const int32_t* row, int n, int v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (row[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-__device__ inline int upper_bound_i32(const int32_t* row, int n, int v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (row[mid] <= v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
+// Rows of up to SEG_LDS ids are searched in LDS (one coalesced load per
+// block instead of a chain of dependent global loads); longer rows are
+// searched in global memory.
+constexpr int SEG_LDS = 4096;
 
-__global__ void seg_prep_kernel(const FwdParams p, int bm) {
+struct SegRow {
+  const int32_t* g;
+  const int32_t* l;  // LDS copy or nullptr
+  int n;
+  __device__ int at(int i) const { return l ? l[i] : g[i]; }
+  __device__ int lower(int v) const {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (at(mid) < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  }
+  __device__ int upper(int v) const {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (at(mid) <= v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  }
+};
+
+// grid (max(n_qt, ceil(Sk / 256)), B), 256 threads.  Block x handles query
+// tile x (if any) and keys [256 x, 256 x + 256) (derived key positions).
+__global__ __launch_bounds__(256) void seg_prep_kernel(const FwdParams p, int bm) {
+  __shared__ int32_t sk_l[SEG_LDS];
+  __shared__ int32_t sq_l[SEG_LDS];
   __shared__ int s_min_lo, s_max_hi, s_max_lo, s_min_hi;
-  const int qt = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int bx = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int32_t* sq = p.seg_q + b * p.seg_q_sb;
+  const int32_t* sk = p.seg_k + b * p.seg_k_sb;
+  const bool same = sq == sk && p.Sq == p.Sk;
+  const bool k_lds = p.Sk <= SEG_LDS, q_lds = !same && p.Sq <= SEG_LDS;
+  if (k_lds)
+    for (int i = t; i < p.Sk; i += blockDim.x) sk_l[i] = sk[i];
+  if (q_lds)
+    for (int i = t; i < p.Sq; i += blockDim.x) sq_l[i] = sq[i];
   if (t == 0) {
     s_min_lo = INT_MAX; s_max_hi = INT_MIN; s_max_lo = INT_MIN; s_min_hi = INT_MAX;
   }
   __syncthreads();
-  const int32_t* sq = p.seg_q + b * p.seg_q_sb;
-  const int32_t* sk = p.seg_k + b * p.seg_k_sb;
-  for (int i = qt * bm + t; i < min((qt + 1) * bm, p.Sq); i += blockDim.x) {
-    const int id = sq[i];
+  const SegRow K{sk, k_lds ? sk_l : nullptr, p.Sk};
+  const SegRow Q = same ? K : SegRow{sq, q_lds ? sq_l : nullptr, p.Sq};
+
+  // key positions: index within the key's run of equal ids
+  if (p.kpos_ws) {
+    const int j = bx * 256 + t;
+    if (j < p.Sk) p.kpos_ws[(int64_t)b * p.Sk + j] = j - K.lower(K.at(j));
+  }
+  if (bx >= p.n_qt) return;  // uniform per block
+  const int i = bx * bm + t;
+  if (t < bm && i < p.Sq) {
+    const int id = Q.at(i);
     int lo = 0, hi = 0;
     if (id >= 0) {
-      lo = lower_bound_i32(sk, p.Sk, id);
-      hi = upper_bound_i32(sk, p.Sk, id);
+      lo = K.lower(id);
+      hi = K.upper(id);
     }
     p.q_range[(int64_t)b * p.Sq + i] = make_int2(lo, hi);
-    if (p.qpos_ws) p.qpos_ws[(int64_t)b * p.Sq + i] = i - lower_bound_i32(sq, p.Sq, id);
+    if (p.qpos_ws) p.qpos_ws[(int64_t)b * p.Sq + i] = i - Q.lower(id);
     if (hi > lo) {
       atomicMin(&s_min_lo, lo);
       atomicMax(&s_max_hi, hi);
@@ -83,7 +114,7 @@ __global__ void seg_prep_kernel(const FwdParams p, int bm) {
       r.w = s_min_hi / FWD_BN;
       if (r.w < r.z) r.w = r.z;
     }
-    p.qt_range[(int64_t)b * p.n_qt + qt] = r;
+    p.qt_range[(int64_t)b * p.n_qt + bx] = r;
   }
 }
 
@@ -92,12 +123,8 @@ __global__ void seg_prep_kernel(const FwdParams p, int bm) {
 // key, instead of once per query tile that visits it).
 // ---------------------------------------------------------------------------
 __device__ inline int key_position(const FwdParams& p, int b, int j) {
-  if (p.pos_k_mode == POS_ARRAY) return p.pos_k[b * p.pos_k_sb + j];
-  if (p.pos_k_mode == POS_SEGMENT) {
-    const int32_t* sk = p.seg_k + b * p.seg_k_sb;
-    return j - lower_bound_i32(sk, p.Sk, sk[j]);
-  }
-  return j;
+  if (p.pos_k_mode == POS_ARANGE) return j;
+  return p.pos_k[b * p.pos_k_sb + j];  // user array, or derived by seg_prep_kernel
 }
 
 __device__ inline int query_position(const FwdParams& p, int b, int i) {
@@ -105,25 +132,22 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
   return p.pos_q[b * p.pos_q_sb + i];
 }
 
+// One thread per 8 consecutive elements (4 pairs) of a K row.
 template <typename T>
-__global__ void k_rotate16_kernel(const FwdParams p) {
-  const int half = p.D / 2;
-  const int rows_per_blk = blockDim.x / half;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_blk + threadIdx.x / half;
-  const int i = threadIdx.x % half;
+__global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
+  const int q8 = p.D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-  if (row >= nrows) return;
+  if (idx >= nrows * q8) return;
+  const int64_t row = idx / q8;
+  const int d0 = (int)(idx % q8) * 8;
   const int j = (int)(row % p.Sk);
   const int hk = (int)((row / p.Sk) % p.n_rot_kv);
   const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
-  const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + 2 * i;
-  const uint32_t w = *(const uint32_t*)src;
-  const float a = Elem<T>::to_f32((uint16_t)(w & 0xFFFF));
-  const float c = Elem<T>::to_f32((uint16_t)(w >> 16));
-  const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.log2_base);
-  const float ra = fmaf(a, cs.x, -c * cs.y);
-  const float rc = fmaf(c, cs.x, a * cs.y);
-  ((uint32_t*)p.k_rot)[row * half + i] = Elem<T>::pack2(ra, rc);
+  const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + d0;
+  const uint4 x = *(const uint4*)src;
+  const uint4 r = rope_quad<T>(x, p.rope_tab, p.rope_tab_len, key_position(p, b, j), d0, p.D, p.log2_base);
+  *(uint4*)((uint16_t*)p.k_rot + row * p.D + d0) = r;
 }
 
 __global__ void k_rotate32_kernel(const FwdParams p) {
@@ -199,44 +223,90 @@ __global__ void mask_tiles_kernel(const FwdParams p, int bm) {
 // the output O^T = V^T P^T is rescaled lane-locally.  P^T leaves the
 // accumulator registers directly as the B operand of the P.V MFMA; V^T comes
 // from LDS through the transposing read.
+//
+// Q is pre-multiplied by scale * log2(e) before rounding to the MFMA type,
+// so scores arrive in the log2 domain.  The running max is raised only when
+// a new score exceeds it by more than 2^8 (otherwise exponentials stay below
+// 256 and nothing is rescaled); numerator and denominator always share the
+// same reference, so the result is the same softmax.
+//
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+constexpr float LAZY_RESCALE_LOG2 = 8.0f;
+
+// LDS row layout of the K and V tiles: K rows D + 8 elements apart, V rows
+// D + 32 apart.  With 64 four-byte banks, the 16 K rows one operand fetch
+// touches (same 16-byte chunk) then start 4 banks apart, and the 4 V rows a
+// transposing read touches (64 bytes each per pair of lane groups) 16 banks
+// apart, so neither access has bank conflicts.
+template <int D> struct Lay {
+  static constexpr int KS = D + 8, VS = D + 32;
+};
+
+// Tile class bytes kept in LDS (boolean-mask mode) when the key axis has at
+// most this many tiles; longer rows read them from global memory.
+constexpr int CLS_LDS = 4096;
+
+template <typename T, int D, int MK>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   constexpr int BM = FWD_BM, BN = FWD_BN;
-  constexpr int KS = D + 8;   // LDS row stride (elements) of K
-  constexpr int VS = D + 16;  // LDS row stride (elements) of V
   constexpr int NS = D / 16;  // k-steps of K Q^T
   constexpr int ND = D / 32;  // 32-row d blocks of O^T
-  constexpr int CH = D / 8;   // 16-byte chunks per row
-  constexpr int RPP = 256 / CH;
-  constexpr int NP = BN / RPP;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * VS];
+  constexpr int CH = D / 8;   // 16-byte chunks of data per row
+  constexpr int KS = Lay<D>::KS, VS = Lay<D>::VS;
+  constexpr int KCH = KS / 8, VCH = VS / 8;  // 16-byte slots per padded row
+  // one direct-to-LDS wave instruction fills 64 consecutive slots (1 KB);
+  // a padded tile of 64 rows takes KCH (VCH) of them
+  constexpr int KINS = KCH, VINS = VCH;
+  constexpr int KPW = (KINS + 3) / 4, VPW = (VINS + 3) / 4;  // per wave, at most
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * VS];
+  __shared__ uint8_t cls_lds[MK == 1 ? CLS_LDS : 1];
 
+  // work order: (kv-head, b, query tile, head within the group).  The G
+  // heads that share K/V run side by side and long tiles start first; the
+  // contiguous range each XCD receives covers whole kv-heads, so their K/V
+  // stay in that XCD's L2, and batches mix within every XCD.
   const int nwork = p.B * p.Hq * p.n_qt;
   const int w = xcd_remap(blockIdx.x, nwork);
-  const int qt = w % p.n_qt;
-  const int bh = w / p.n_qt;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int hk = h / p.G;
+  const int g = w % p.G;
+  const int qt = (w / p.G) % p.n_qt;
+  const int kvb = w / (p.G * p.n_qt);
+  const int b = kvb % p.B, hk = kvb / p.B;
+  const int h = hk * p.G + g;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int qi = qt * BM + wave * 32 + l32;
   const bool qvalid = qi < p.Sq;
 
-  // ---- Q fragment: B operand of S^T = K Q^T (query l32, d = s*16 + hh*8 + e)
+  // ---- Q fragment, pre-scaled: B operand of S^T = K Q^T
   uint4 qf[NS];
   {
     const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
     const bool rot = h < p.n_rot;
     const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
+    const float sc = p.scale_log2;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (qvalid) {
         x = *(const uint4*)(qrow + s * 16 + hh * 8);
-        if (rot) x = rope_quad<T>(x, p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8, D, p.log2_base);
+        uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+        const int d0 = s * 16 + hh * 8;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float a = Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF));
+          float c = Elem<T>::to_f32((uint16_t)(wv[t] >> 16));
+          if (rot) {
+            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, d0 / 2 + t, D, p.log2_base);
+            const float ra = fmaf(a, cs.x, -c * cs.y);
+            const float rc = fmaf(c, cs.x, a * cs.y);
+            a = ra;
+            c = rc;
+          }
+          wv[t] = Elem<T>::pack2(a * sc, c * sc);
+        }
+        x = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
       qf[s] = x;
     }
@@ -260,7 +330,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   int lo = 0, hi = p.Sk;
   const uint8_t* cls_row = nullptr;
   const uint8_t* mrow = nullptr;
-  if (p.mask_kind == 2) {
+  bool cls_in_lds = false;
+  if constexpr (MK == 2) {
     const int4 r = p.qt_range[(int64_t)b * p.n_qt + qt];
     kt_beg = r.x; kt_end = r.y; full_beg = r.z; full_end = r.w;
     if (qvalid) {
@@ -269,33 +340,82 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
     } else {
       lo = 0; hi = 0;
     }
-  } else if (p.mask_kind == 1) {
+  } else if constexpr (MK == 1) {
     const int bm_ = p.Bm == 1 ? 0 : b, hm_ = p.Hm == 1 ? 0 : h;
     cls_row = p.tile_cls + ((int64_t)(bm_ * p.Hm + hm_) * p.n_qt + qt) * p.n_kt;
     if (qvalid) mrow = p.mask + b * p.ms[0] + h * p.ms[1] + (int64_t)qi * p.ms[2];
-  }
-  const int first_tail_tile = p.Sk / BN;  // tiles from here on reach past Sk
-
-  uint4 kreg[NP], vreg[NP];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int r = pp * RPP + tid / CH, c = tid % CH;
-      const int key = kt * BN + r;
-      if (key < p.Sk) {
-        kreg[pp] = *(const uint4*)(kbase + (int64_t)key * kstride + c * 8);
-        vreg[pp] = *(const uint4*)(vbase + (int64_t)key * vstride + c * 8);
-      } else {
-        kreg[pp] = make_uint4(0, 0, 0, 0);
-        vreg[pp] = make_uint4(0, 0, 0, 0);
-      }
+    cls_in_lds = p.n_kt <= CLS_LDS;
+    if (cls_in_lds) {
+      for (int i = tid; i < p.n_kt; i += 256) cls_lds[i] = cls_row[i];
+      __syncthreads();
     }
+  }
+  auto cls_at = [&](int kt) -> int {
+    if constexpr (MK == 1) return cls_in_lds ? cls_lds[kt] : cls_row[kt];
+    return 1;
   };
   auto next_live = [&](int kt) {
-    if (cls_row) {
-      while (kt < kt_end && cls_row[kt] == 0) ++kt;
+    if constexpr (MK == 1) {
+      while (kt < kt_end && cls_at(kt) == 0) ++kt;
     }
     return kt;
+  };
+  const int first_tail_tile = p.Sk / BN;  // tiles from here on reach past Sk
+
+  // ---- direct-to-LDS tile loads.  Slot q of a padded tile is row q / KCH,
+  // chunk q % KCH; pad slots (chunk >= CH) load chunk 0 of their row again.
+  // The per-lane element offsets within a tile are fixed (row strides are
+  // below 2^24 elements, so they fit 32 bits); only the last tile, whose
+  // rows past Sk load row Sk - 1 instead (their keys are masked), needs
+  // them recomputed.
+  uint32_t koff[KPW], voff[KPW > VPW ? KPW : VPW];
+  auto slot_off = [&](int ins, int nch, int64_t stride, int key0, bool clamp) -> uint32_t {
+    const int q = ins * 64 + lane;
+    int row = q / nch;
+    if (clamp) row = min(key0 + row, p.Sk - 1) - key0;
+    const int ch = q % nch;
+    return (uint32_t)(row * stride + (ch < CH ? ch : 0) * 8);
+  };
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave, KCH, kstride, 0, false);
+#pragma unroll
+  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave, VCH, vstride, 0, false);
+  auto load_kv = [&](int kt, int stage) {
+    const int key0 = kt * BN;
+    const uint16_t* ktb = kbase + (int64_t)key0 * kstride;
+    const uint16_t* vtb = vbase + (int64_t)key0 * vstride;
+    uint16_t* kdst = &Ks[stage][0];
+    uint16_t* vdst = &Vs[stage][0];
+    if (key0 + BN <= p.Sk) {
+#pragma unroll
+      for (int u = 0; u < KPW; ++u)
+        if (u * 4 + wave < KINS) lds_dma16(ktb + koff[u], kdst + (u * 4 + wave) * 512);
+#pragma unroll
+      for (int u = 0; u < VPW; ++u)
+        if (u * 4 + wave < VINS) lds_dma16(vtb + voff[u], vdst + (u * 4 + wave) * 512);
+    } else {
+#pragma unroll
+      for (int u = 0; u < KPW; ++u)
+        if (u * 4 + wave < KINS)
+          lds_dma16(ktb + slot_off(u * 4 + wave, KCH, kstride, key0, true), kdst + (u * 4 + wave) * 512);
+#pragma unroll
+      for (int u = 0; u < VPW; ++u)
+        if (u * 4 + wave < VINS)
+          lds_dma16(vtb + slot_off(u * 4 + wave, VCH, vstride, key0, true), vdst + (u * 4 + wave) * 512);
+    }
+  };
+
+  // ---- S^T = K Q^T + cinit of one tile (log2 domain)
+  auto qk = [&](int stage, f32x16_t (&sacc)[2], const f32x16_t& c0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + l32;
+        const uint4 a = *(const uint4*)&Ks[stage][row * KS + (2 * s + hh) * 8];
+        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? c0 : sacc[kb]);
+      }
+    }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -307,62 +427,74 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
 
   const int grp = lane >> 4, gi = lane & 15, rr = gi >> 2, cc = gi & 3;
 
+  // Pipeline: tile j's K and V sit in stage j % 2 while tile j + 1's K and V
+  // stream into the other stage.  One barrier per tile: after it, every
+  // wave is done with tile j - 1 (the stage the next loads overwrite) and
+  // tile j has landed.
   int kt = next_live(kt_beg);
-  if (kt < kt_end) load_tile(kt);
+  if (kt < kt_end) load_kv(kt, 0);
+  int j = 0;
+  // scores come out of the MFMA already shifted by -m (the accumulator
+  // starts at -m instead of 0); cinit changes only when m does
+  f32x16_t cinit = {};
   while (kt < kt_end) {
+    const int stage = __builtin_amdgcn_readfirstlane(j & 1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int r = pp * RPP + tid / CH, c = tid % CH;
-      *(uint4*)&Ks[r * KS + c * 8] = kreg[pp];
-      *(uint4*)&Vs[r * VS + c * 8] = vreg[pp];
-    }
-    __syncthreads();
-    const int kt_next = next_live(kt + 1);
-    if (kt_next < kt_end) load_tile(kt_next);
+    const int kt1 = next_live(kt + 1);
+    if (kt1 < kt_end) load_kv(kt1, stage ^ 1);
+    f32x16_t scur[2];
+    qk(stage, scur, cinit);
 
+    // ---- remove non-live keys (boundary tiles only)
     bool check;
-    if (p.mask_kind == 2) check = !(kt >= full_beg && kt < full_end);
-    else if (p.mask_kind == 1) check = cls_row[kt] == 2 || kt >= first_tail_tile;
+    if constexpr (MK == 2) check = !(kt >= full_beg && kt < full_end);
+    else if constexpr (MK == 1) check = cls_at(kt) == 2 || kt >= first_tail_tile;
     else check = kt >= first_tail_tile;
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16_t sacc[2];
+    if (check) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint4 a = *(const uint4*)&Ks[(kb * 32 + l32) * KS + s * 16 + hh * 8];
-        sacc[kb] = mfma32<T>(a, qf[s], sacc[kb]);
-      }
-    }
-
-    // ---- scale into the log2 domain; remove non-live keys
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = sacc[kb][v] * p.scale_log2;
-        if (check) {
+        for (int v = 0; v < 16; ++v) {
           const int key = kt * BN + kb * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
           bool live;
-          if (p.mask_kind == 2) live = key >= lo && key < hi;
-          else if (p.mask_kind == 1) live = key < p.Sk && mrow != nullptr && mrow[key] != 0;
+          if constexpr (MK == 2) live = key >= lo && key < hi;
+          else if constexpr (MK == 1) live = key < p.Sk && mrow != nullptr && mrow[key] != 0;
           else live = key < p.Sk;
-          x = live ? x : -INFINITY;
+          scur[kb][v] = live ? scur[kb][v] : -INFINITY;
         }
-        sacc[kb][v] = x;
-        mx = fmaxf(mx, x);
       }
     }
-    mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float ls = 0.f;
+
+    // ---- online softmax with lazy rescaling.  scur holds s - m_use, where
+    // m_use is the running reference (0 before any live key).  The reference
+    // moves only when a score exceeds it by more than 2^8.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, scur[kb][v]), scur[kb][v + 1]);
+    mx = half_swap_max(mx);
+    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx > LAZY_RESCALE_LOG2;
+    if (__any(need)) {
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      const float delta = need ? mx : 0.f;
+      const float m_new = need ? m_use + delta : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) scur[kb][v] -= delta;
+      const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cinit[v] = nm;
+    }
     uint4 pk[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -371,41 +503,36 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
         uint32_t wv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(sacc[kb][jj * 8 + 2 * e] - m_use);
-          const float p1 = fast_exp2(sacc[kb][jj * 8 + 2 * e + 1] - m_use);
-          ls += p0 + p1;
+          const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e]);
+          const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1]);
+          l_run += p0 + p1;
           wv[e] = Elem<T>::pack2(p0, p1);
         }
         pk[kb][jj] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
     }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int row0 = kb * 32 + jj * 16 + 4 * hh + rr;
-          const uint2 a0 = lds_read_tr<T>(&Vs[row0 * VS + col]);
-          const uint2 a1 = lds_read_tr<T>(&Vs[(row0 + 8) * VS + col]);
+        for (int db = 0; db < ND; ++db) {
+          const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
+          const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
+          const uint2 a0 = lds_read_tr<T>(&Vs[stage][r0 * VS + col]);
+          const uint2 a1 = lds_read_tr<T>(&Vs[stage][(r0 + 8) * VS + col]);
           oacc[db] = mfma32<T>(make_uint4(a0.x, a0.y, a1.x, a1.y), pk[kb][jj], oacc[db]);
         }
       }
     }
-    kt = kt_next;
+    kt = kt1;
+    ++j;
   }
 
   // ---- epilogue: O = O^T / l, lse
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
     uint16_t* orow = (uint16_t*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)qi * p.os[2];
@@ -559,20 +686,40 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
     rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p.rope_tab, p.rope_tab_len, p.D,
                                                                               p.log2_base);
   }
-  if (p.mask_kind == 2) seg_prep_kernel<<<dim3(p.n_qt, p.B), dim3(bm), 0, s>>>(p, bm);
+  if (p.mask_kind == 2) {
+    const int nkb = (p.Sk + 255) / 256;
+    seg_prep_kernel<<<dim3(p.n_qt > nkb ? p.n_qt : nkb, p.B), dim3(256), 0, s>>>(p, bm);
+  }
   if (p.n_rot_kv > 0) {
-    const int rows_per_blk = 256 / (p.D / 2);
     const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-    const unsigned nblk = (unsigned)((nrows + rows_per_blk - 1) / rows_per_blk);
-    if (f32) k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
-    else if (p.dtype == 2) k_rotate16_kernel<BF16><<<dim3(nblk), dim3(256), 0, s>>>(p);
-    else k_rotate16_kernel<F16><<<dim3(nblk), dim3(256), 0, s>>>(p);
+    if (f32) {
+      const int rows_per_blk = 256 / (p.D / 2);
+      const unsigned nblk = (unsigned)((nrows + rows_per_blk - 1) / rows_per_blk);
+      k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
+    } else {
+      const unsigned nblk = (unsigned)((nrows * (p.D / 8) + 255) / 256);
+      if (p.dtype == 2) k_rotate16_kernel<BF16><<<dim3(nblk), dim3(256), 0, s>>>(p);
+      else k_rotate16_kernel<F16><<<dim3(nblk), dim3(256), 0, s>>>(p);
+    }
   }
   if (p.mask_kind == 1) {
     const int64_t ntiles = (int64_t)p.Bm * p.Hm * p.n_qt * p.n_kt;
     mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static void launch_mfma_d(const FwdParams& p, unsigned nwork, hipStream_t s) {
+  if (p.mask_kind == 2) fwd_mfma_kernel<T, D, 2><<<dim3(nwork), dim3(256), 0, s>>>(p);
+  else if (p.mask_kind == 1) fwd_mfma_kernel<T, D, 1><<<dim3(nwork), dim3(256), 0, s>>>(p);
+  else fwd_mfma_kernel<T, D, 0><<<dim3(nwork), dim3(256), 0, s>>>(p);
+}
+
+template <typename T>
+static void launch_mfma(const FwdParams& p, unsigned nwork, hipStream_t s) {
+  if (p.D == 64) launch_mfma_d<T, 64>(p, nwork, s);
+  else launch_mfma_d<T, 128>(p, nwork, s);
 }
 
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
@@ -582,11 +729,9 @@ hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
     if (p.D == 64) fwd_f32_kernel<64><<<dim3(nwork), dim3(64), 0, s>>>(p);
     else fwd_f32_kernel<128><<<dim3(nwork), dim3(64), 0, s>>>(p);
   } else if (p.dtype == 2) {
-    if (p.D == 64) fwd_mfma_kernel<BF16, 64><<<dim3(nwork), dim3(256), 0, s>>>(p);
-    else fwd_mfma_kernel<BF16, 128><<<dim3(nwork), dim3(256), 0, s>>>(p);
+    launch_mfma<BF16>(p, nwork, s);
   } else {
-    if (p.D == 64) fwd_mfma_kernel<F16, 64><<<dim3(nwork), dim3(256), 0, s>>>(p);
-    else fwd_mfma_kernel<F16, 128><<<dim3(nwork), dim3(256), 0, s>>>(p);
+    launch_mfma<F16>(p, nwork, s);
   }
   return hipGetLastError();
 }

@@ -12,6 +12,9 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 #define MZ_LDS __attribute__((address_space(3)))
 
@@ -29,8 +32,10 @@ template <> struct Elem<BF16> {
     __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(uint16_t, h);
   }
+  // two values, round to nearest even, one v_cvt_pk_bf16_f32
   __device__ static inline uint32_t pack2(float a, float b) {
-    return static_cast<uint32_t>(from_f32(a)) | (static_cast<uint32_t>(from_f32(b)) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
 };
 template <> struct Elem<F16> {
@@ -41,8 +46,10 @@ template <> struct Elem<F16> {
     _Float16 h = static_cast<_Float16>(x);
     return __builtin_bit_cast(uint16_t, h);
   }
+  // two values, round to nearest even, one v_cvt_pk_f16_f32
   __device__ static inline uint32_t pack2(float a, float b) {
-    return static_cast<uint32_t>(from_f32(a)) | (static_cast<uint32_t>(from_f32(b)) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
   }
 };
 
@@ -87,22 +94,45 @@ template <> __device__ inline uint2 lds_read_tr<F16>(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// 16-byte global -> LDS copy without a register round trip: lane i of the
+// wave writes its 16 bytes to lds_base + 16 * i (lds_base is wave-uniform).
+__device__ inline void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float wave_xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
+// Combine a value with the one held by lane l ^ 32 without going through
+// LDS: v_permlane32_swap exchanges the two 32-lane halves of a pair of
+// registers, so each lane ends up holding its own value and its partner's.
+__device__ inline float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- rotary embedding angles -----------------------------------------------
 // Angle of pair i at position p is p * base^(-2i/D), evaluated in fp64 and
-// rounded to fp32 cos / sin at the end.  The table holds positions
-// [0, tab_len); other positions take the same fp64 formula directly, so both
-// routes give identical bits.
+// rounded to fp32 cos / sin at the end.  The angle is first reduced to
+// [-pi, pi] by subtracting the nearest multiple of 2*pi (2*pi split in two
+// doubles, Cody-Waite), so the fp64 sine / cosine only see small arguments.
+// The table holds positions [0, tab_len); other positions take the same
+// formula directly, so both routes give identical bits.
 __device__ inline float2 rope_cs_direct(int pos, int i, int D, double log2_base) {
-  double theta = exp2(-(double)(2 * i) / (double)D * log2_base);
-  double ang = (double)pos * theta;
+  const double theta = exp2(-(double)(2 * i) / (double)D * log2_base);
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0.15915494309189533577);  // 1 / (2 pi)
+  double r = fma(-k, 6.28318530717958623200, ang);     // 2 pi, high part
+  r = fma(-k, 2.44929359829470635445e-16, r);           // 2 pi, low part
   double s, c;
-  sincos(ang, &s, &c);
+  sincos(r, &s, &c);
   return make_float2((float)c, (float)s);
 }
 

@@ -34,7 +34,7 @@ struct FwdParams {
   int pos_q_mode, pos_k_mode;
   const int32_t* pos_q;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
   int64_t pos_q_sb;
-  const int32_t* pos_k;  // user array (POS_ARRAY); segment-derived on the fly
+  const int32_t* pos_k;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
   int64_t pos_k_sb;
   float2* rope_tab;
   int rope_tab_len;
@@ -52,6 +52,7 @@ struct FwdParams {
   int2* q_range;   // [B][Sq] live key range of each query
   int4* qt_range;  // [B][n_qt] (first tile, end tile, first full tile, end full tile)
   int32_t* qpos_ws;  // [B][Sq] derived query positions
+  int32_t* kpos_ws;  // [B][Sk] derived key positions
   float* lse;
 };
 
@@ -77,7 +78,6 @@ struct DecodeParams {
   double log2_base;
   int rope;
   // workspace
-  uint32_t* counters;  // [B][Hkv]
   float2* part_ml;     // [B][Hkv][n_chunks][R]   (m in log2 units, l)
   float* part_acc;     // [B][Hkv][n_chunks][R][D]
 };

@@ -233,3 +233,25 @@ def test_decode_matches_fwd_single_query():
     of = run_fwd(f)
     st = mzref.parity_stats(to64(od), to64(of))
     assert mzref.within_tolerance("bf16", st), st
+
+
+def test_plan_then_execute_equals_fwd():
+    import masked_bidirectional_attention_amd as mz
+    case = W.random_fwd(30, 1, 8, 2, 500, 500, 128, "bf16", W.MASK_SEGMENT, rope_base=1e6, n_segments=3)
+    a = run_fwd(case)
+    call = mz.FwdCall(dev(case.q), dev(case.k), dev(case.v), seg_q=dev(case.seg_q), seg_k=dev(case.seg_k),
+                      rope_base=case.rope_base)
+    call.plan()
+    call.execute()
+    call.execute()  # executing again over the same plan is allowed
+    torch.cuda.synchronize()
+    assert torch.equal(call.out, a)
+
+
+@pytest.mark.parametrize("S", [4096, 5000])
+def test_long_segment_rows_fwd(S):
+    """Segment rows longer than the LDS search buffer take the global path."""
+    case = W.random_fwd(31, 1, 2, 1, S, S, 64, "bf16", W.MASK_SEGMENT, rope_base=1e4, n_segments=4)
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity("bf16", o, ref, f"long segments S={S}")
