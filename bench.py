@@ -52,6 +52,87 @@ def decode_bytes(L=8192, span=8192):
     return 2 * 2 * L * 128 * 2 * 2 + 2 * span + 2 * (2 * 16 * 128 * 2)
 
 
+def kernel_source_hash():
+    """Hash of the kernel sources; counter-derived traffic is reported only
+    while it matches the hash recorded with the counters."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "masked_bidirectional_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+COPY_BYTES = 64 * 1024 * 1024
+
+
+def pmc_workload():
+    """A short run for rocprofv3 --pmc: a plain copy of known size (the
+    counter calibration), then the attention kernel and the decode step of
+    the timed workload, three launches each."""
+    import torch
+    import masked_bidirectional_attention_amd as mz
+    from masked_bidirectional_attention_amd import workloads as W
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    c3 = W.qwen_cfg_packed()
+    seg = c3.seg_q.to(dev)
+    fwd = mz.FwdCall(c3.q.to(dev), c3.k.to(dev), c3.v.to(dev), seg_q=seg, seg_k=seg, rope_base=c3.rope_base)
+    c4 = W.vox_decode(8192)
+    dq, dmask = c4.q.to(dev), c4.mask.to(dev)
+    copies = [(c4.k_cache.to(dev), c4.v_cache.to(dev)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        fwd.plan()
+        fwd.execute()
+    torch.cuda.synchronize()
+    for kc, vc in copies:
+        mz.mzattn_decode(dq, kc, vc, span=8192, mask=dmask, scale=c4.scale)
+    torch.cuda.synchronize()
+    print("pmc workload done", flush=True)
+
+
+def traffic_from(fetch_dir, write_dir):
+    """HBM bytes per launch from two rocprofv3 --pmc runs of pmc_workload
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each divided by the
+    factor the same counter shows for the copy kernel of known size."""
+    import csv
+
+    def per_kernel(d, counter):
+        vals = {}
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, fn)) as f:
+                        for r in csv.DictReader(f):
+                            if r["Counter_Name"] == counter:
+                                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copy = [v for k, vs in vals.items() if "copy" in k.lower() or "elementwise" in k.lower() for v in vs]
+        if not copy:
+            raise SystemExit(f"no copy kernel found for {counter} in {d}")
+        factor = max(copy) * 1024.0 / COPY_BYTES
+        out[counter.lower() + "_factor"] = round(factor, 4)
+        for key, pat in (("fwd_mfma_kernel", "fwd_mfma_kernel"), ("decode_mfma_kernel", "decode_mfma_kernel"),
+                         ("decode_merge16_kernel", "decode_merge16_kernel")):
+            vs = [v for k, v_ in vals.items() if pat in k for v in v_]
+            if vs:
+                out.setdefault(key, {})[counter.lower() + "_bytes"] = round(sum(vs) / len(vs) * 1024.0 / factor)
+    for key in ("fwd_mfma_kernel", "decode_mfma_kernel", "decode_merge16_kernel"):
+        if key in out and "fetch_size_bytes" in out[key] and "write_size_bytes" in out[key]:
+            out[key]["bytes"] = out[key]["fetch_size_bytes"] + out[key]["write_size_bytes"]
+    return out
+
+
 def cpu_baseline():
     import threadpoolctl
     from masked_bidirectional_attention_amd import workloads as W
@@ -91,11 +172,22 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch (from rocprofv3 --pmc), if present")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run the short counter workload (under rocprofv3 --pmc) and exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output dirs into traffic JSON on stdout and exit")
     a = ap.parse_args(argv)
+    if a.traffic_from:
+        print(json.dumps(traffic_from(*a.traffic_from), indent=1))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if a.pmc_workload:
+        pmc_workload()
+        return 0
 
     import torch
     import masked_bidirectional_attention_amd as mz
@@ -115,7 +207,7 @@ def main(argv=None):
     dq, dmask = c4.q.to(dev), c4.mask.to(dev)
     kc0, vc0 = c4.k_cache.to(dev), c4.v_cache.to(dev)
     copies = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(max(0, a.cache_copies - 1))]
-    dout = torch.empty_like(dq)
+    dec = mz.DecodeCall(dq, kc0, vc0, span=8192, mask=dmask, scale=c4.scale)
     torch.cuda.synchronize()
     print(f"[bench] device {props.name}, {props.multi_processor_count} CUs; inputs resident", file=sys.stderr, flush=True)
 
@@ -126,8 +218,8 @@ def main(argv=None):
         fwd.execute()
         if evs:
             evs[1].record()
-        kc, vc = copies[i % len(copies)]
-        mz.mzattn_decode(dq, kc, vc, span=8192, mask=dmask, scale=c4.scale, out=dout)
+        dec.set_cache(*copies[i % len(copies)])
+        dec()
         if evs:
             evs[2].record()
 
@@ -154,6 +246,8 @@ def main(argv=None):
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
             traffic = json.load(f)
+        if traffic.get("source_hash") != kernel_source_hash():
+            traffic = {}  # the kernels changed since the counters were taken
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -183,7 +277,7 @@ def main(argv=None):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic.get("fwd_mfma_kernel"),
+            "traffic": (traffic.get("fwd_mfma_kernel") or {}).get("bytes"),
             "kernel_us": round(fwd_ms * 1e3, 2),
             "algorithmic_gflop": round(fwd_flops() / 1e9, 3),
         },
@@ -197,7 +291,7 @@ def main(argv=None):
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                "traffic": traffic.get("decode_mfma_kernel"),
+                "traffic": (traffic.get("decode_mfma_kernel") or {}).get("bytes"),
                 "kernel_us": round(dec_ms * 1e3, 2),
                 "algorithmic_mb": round(decode_bytes() / 1e6, 3),
             },

@@ -6,6 +6,7 @@ The compute lives in ``libmzattn.so`` (hand-written HIP, C ABI declared in
     from masked_bidirectional_attention_amd import mzattn_fwd, mzattn_decode
 """
 from ._binding import (  # noqa: F401
+    DecodeCall,
     FwdCall,
     LIB_PATH,
     MzattnError,
@@ -15,4 +16,4 @@ from ._binding import (  # noqa: F401
     mzattn_fwd,
 )
 
-__all__ = ["FwdCall", "mzattn_fwd", "mzattn_decode", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]
+__all__ = ["DecodeCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]

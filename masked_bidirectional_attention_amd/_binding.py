@@ -332,6 +332,63 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=
                    return_lse=return_lse, workspace=workspace, stream=stream)()
 
 
+class DecodeCall:
+    """A marshalled static-cache step: the C argument struct plus the
+    tensors it points to.  ``set_cache`` swaps in other caches of the same
+    shape, strides and dtype; ``__call__`` launches on the call's stream."""
+
+    def __init__(self, q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
+                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, out=None,
+                 workspace=None, stream=None):
+        torch = _torch()
+        L = lib()
+        B, Hq, T, D = q.shape
+        Hkv, C = k_cache.shape[1], k_cache.shape[2]
+        a = new_decode_args()
+        a.dtype = _dtype_code(q)
+        if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+            raise MzattnError(MZ_ERR_DTYPE, "q and the caches must share one dtype")
+        a.batch, a.heads_q, a.heads_kv, a.q_len, a.head_dim, a.cache_len = B, Hq, Hkv, T, D, C
+        a.span = C if span is None else int(span)
+        a.scale = float(scale)
+        a.rope_base = float(rope_base)
+        o = out if out is not None else torch.empty(B, Hq, T, D, dtype=q.dtype, device=q.device)
+        a.q, a.k_cache, a.v_cache, a.o = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr()
+        a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k_cache, "k_cache")
+        a.v_stride, a.o_stride = _strides3(v_cache, "v_cache"), _strides3(o, "o")
+        keep = [q, k_cache, v_cache, o]
+        if mask is not None:
+            m, st = _mask_strides(mask, B, Hq, T, C)
+            a.mask, a.mask_stride = m.data_ptr(), st
+            keep.append(m)
+        if q_pos is not None:
+            if q_pos.dtype != torch.int32 or q_pos.dim() != 2:
+                raise MzattnError(MZ_ERR_DTYPE, "q_pos must be int32 [B, q_len]")
+            a.q_pos = q_pos.data_ptr()
+            a.q_pos_stride_b = q_pos.stride(0) if q_pos.shape[0] > 1 else 0
+            keep.append(q_pos)
+        need = ctypes.c_size_t(0)
+        _check(L.mzattn_decode_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        self.stream = torch.cuda.current_stream(q.device) if stream is None else stream
+        if workspace is None:
+            workspace = _WS.get("decode", q.device, self.stream.cuda_stream, need.value, zero=False)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        keep.append(workspace)
+        self.args, self.out, self._keep, self._lib = a, o, keep, L
+        self._cache_shape = (tuple(k_cache.shape), tuple(k_cache.stride()), k_cache.dtype)
+
+    def set_cache(self, k_cache, v_cache):
+        for c in (k_cache, v_cache):
+            if (tuple(c.shape), tuple(c.stride()), c.dtype) != self._cache_shape:
+                raise MzattnError(MZ_ERR_SHAPE, "replacement cache differs in shape, strides or dtype")
+        self.args.k_cache, self.args.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+        self._keep[1], self._keep[2] = k_cache, v_cache
+
+    def __call__(self):
+        _check(self._lib.mzattn_decode(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
+        return self.out
+
+
 def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
                   scale: float = 0.0, rope_base: float = 0.0, q_pos=None, out=None,
                   workspace=None, stream=None):
@@ -339,39 +396,5 @@ def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
     q [B, Hq, q_len, D]; k_cache / v_cache [B, Hkv, cache_len, D]; keys
     [0, span) considered (default: the whole cache); mask: bool
     [B|1, Hq|1, q_len|1, cache_len] or None."""
-    torch = _torch()
-    L = lib()
-    B, Hq, T, D = q.shape
-    Hkv, C = k_cache.shape[1], k_cache.shape[2]
-    a = new_decode_args()
-    a.dtype = _dtype_code(q)
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise MzattnError(MZ_ERR_DTYPE, "q and the caches must share one dtype")
-    a.batch, a.heads_q, a.heads_kv, a.q_len, a.head_dim, a.cache_len = B, Hq, Hkv, T, D, C
-    a.span = C if span is None else int(span)
-    a.scale = float(scale)
-    a.rope_base = float(rope_base)
-    o = out if out is not None else torch.empty(B, Hq, T, D, dtype=q.dtype, device=q.device)
-    a.q, a.k_cache, a.v_cache, a.o = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr()
-    a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k_cache, "k_cache")
-    a.v_stride, a.o_stride = _strides3(v_cache, "v_cache"), _strides3(o, "o")
-    keep = [q, k_cache, v_cache, o]
-    if mask is not None:
-        m, st = _mask_strides(mask, B, Hq, T, C)
-        a.mask, a.mask_stride = m.data_ptr(), st
-        keep.append(m)
-    if q_pos is not None:
-        if q_pos.dtype != torch.int32 or q_pos.dim() != 2:
-            raise MzattnError(MZ_ERR_DTYPE, "q_pos must be int32 [B, q_len]")
-        a.q_pos = q_pos.data_ptr()
-        a.q_pos_stride_b = q_pos.stride(0) if q_pos.shape[0] > 1 else 0
-        keep.append(q_pos)
-    need = ctypes.c_size_t(0)
-    _check(L.mzattn_decode_workspace_size(ctypes.byref(a), ctypes.byref(need)))
-    s = torch.cuda.current_stream(q.device) if stream is None else stream
-    if workspace is None:
-        workspace = _WS.get("decode", q.device, s.cuda_stream, need.value, zero=False)
-    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(L.mzattn_decode(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream)))
-    del keep
-    return o
+    return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
+                      q_pos=q_pos, out=out, workspace=workspace, stream=stream)()

@@ -15,12 +15,15 @@ namespace mz {
 // ---------------------------------------------------------------------------
 // Prepass 1: cos/sin table of the rotary angles, positions [0, len).
 // ---------------------------------------------------------------------------
-__global__ void rope_table_kernel(float2* tab, int len, int D, double log2_base) {
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int len, int D, double log2_base) {
+  __shared__ double theta[64];
   const int half = D / 2;
+  if (threadIdx.x < half) theta[threadIdx.x] = rope_theta(threadIdx.x, D, log2_base);
+  __syncthreads();
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)len * half) return;
   const int pos = (int)(idx / half), i = (int)(idx % half);
-  tab[idx] = rope_cs_direct(pos, i, D, log2_base);
+  tab[idx] = rope_cs_theta(pos, theta[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -34,84 +37,118 @@ __global__ void rope_table_kernel(float2* tab, int len, int D, double log2_base)
 // searched in global memory.
 constexpr int SEG_LDS = 4096;
 
-struct SegRow {
-  const int32_t* g;
-  const int32_t* l;  // LDS copy or nullptr
-  int n;
-  __device__ int at(int i) const { return l ? l[i] : g[i]; }
-  __device__ int lower(int v) const {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (at(mid) < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
+// Binary searches over a non-decreasing id row.  Row is either an LDS array
+// (indexed directly, so the compiler emits LDS reads) or a global pointer.
+template <typename Row>
+__device__ inline int seg_lower(Row row, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < v) lo = mid + 1; else hi = mid;
   }
-  __device__ int upper(int v) const {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (at(mid) <= v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
+  return lo;
+}
+template <typename Row>
+__device__ inline int seg_upper(Row row, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] <= v) lo = mid + 1; else hi = mid;
   }
-};
+  return lo;
+}
+
+template <typename KRow, typename QRow>
+__device__ void seg_prep_body(const FwdParams& p, int bm, int bx, int b, KRow K, QRow Q, int* red) {
+  const int t = threadIdx.x;
+  // key positions: index within the key's run of equal ids
+  if (p.kpos_ws) {
+    const int j = bx * 256 + t;
+    if (j < p.Sk) p.kpos_ws[(int64_t)b * p.Sk + j] = j - seg_lower(K, p.Sk, K[j]);
+  }
+  if (bx >= p.n_qt) return;  // uniform per block
+  const int i = bx * bm + t;
+  // per-lane contributions; lanes without a query give the identities
+  int a0 = INT_MAX, a1 = INT_MIN, a2 = INT_MIN, a3 = INT_MAX;
+  if (t < bm && i < p.Sq) {
+    const int id = Q[i];
+    int lo = 0, hi = 0;
+    if (id >= 0) {
+      lo = seg_lower(K, p.Sk, id);
+      hi = seg_upper(K, p.Sk, id);
+    }
+    p.q_range[(int64_t)b * p.Sq + i] = make_int2(lo, hi);
+    if (p.qpos_ws) p.qpos_ws[(int64_t)b * p.Sq + i] = i - seg_lower(Q, p.Sq, id);
+    const bool live = hi > lo;
+    a0 = live ? lo : INT_MAX;  // min over queries with live keys
+    a1 = live ? hi : INT_MIN;  // max over queries with live keys
+    a2 = live ? lo : 0;        // max over all queries (empty ranges count as 0)
+    a3 = live ? hi : 0;        // min over all queries
+  }
+  // wave-level reductions (every lane takes part), one LDS atomic per wave
+  for (int off = 32; off > 0; off >>= 1) {
+    a0 = min(a0, __shfl_xor(a0, off, 64));
+    a1 = max(a1, __shfl_xor(a1, off, 64));
+    a2 = max(a2, __shfl_xor(a2, off, 64));
+    a3 = min(a3, __shfl_xor(a3, off, 64));
+  }
+  if ((t & 63) == 0) {
+    atomicMin(&red[0], a0);
+    atomicMax(&red[1], a1);
+    atomicMax(&red[2], a2);
+    atomicMin(&red[3], a3);
+  }
+}
 
 // grid (max(n_qt, ceil(Sk / 256)), B), 256 threads.  Block x handles query
 // tile x (if any) and keys [256 x, 256 x + 256) (derived key positions).
 __global__ __launch_bounds__(256) void seg_prep_kernel(const FwdParams p, int bm) {
   __shared__ int32_t sk_l[SEG_LDS];
   __shared__ int32_t sq_l[SEG_LDS];
-  __shared__ int s_min_lo, s_max_hi, s_max_lo, s_min_hi;
+  __shared__ int red[4];
   const int bx = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int32_t* sq = p.seg_q + b * p.seg_q_sb;
   const int32_t* sk = p.seg_k + b * p.seg_k_sb;
   const bool same = sq == sk && p.Sq == p.Sk;
   const bool k_lds = p.Sk <= SEG_LDS, q_lds = !same && p.Sq <= SEG_LDS;
-  if (k_lds)
-    for (int i = t; i < p.Sk; i += blockDim.x) sk_l[i] = sk[i];
-  if (q_lds)
-    for (int i = t; i < p.Sq; i += blockDim.x) sq_l[i] = sq[i];
+  // copy the rows with every load in flight at once (SEG_LDS / 256 each)
+  constexpr int PER = SEG_LDS / 256;
+  if (k_lds) {
+    int32_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) v[u] = t + u * 256 < p.Sk ? sk[t + u * 256] : 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (t + u * 256 < p.Sk) sk_l[t + u * 256] = v[u];
+  }
+  if (q_lds) {
+    int32_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) v[u] = t + u * 256 < p.Sq ? sq[t + u * 256] : 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (t + u * 256 < p.Sq) sq_l[t + u * 256] = v[u];
+  }
   if (t == 0) {
-    s_min_lo = INT_MAX; s_max_hi = INT_MIN; s_max_lo = INT_MIN; s_min_hi = INT_MAX;
+    red[0] = INT_MAX; red[1] = INT_MIN; red[2] = INT_MIN; red[3] = INT_MAX;
   }
   __syncthreads();
-  const SegRow K{sk, k_lds ? sk_l : nullptr, p.Sk};
-  const SegRow Q = same ? K : SegRow{sq, q_lds ? sq_l : nullptr, p.Sq};
-
-  // key positions: index within the key's run of equal ids
-  if (p.kpos_ws) {
-    const int j = bx * 256 + t;
-    if (j < p.Sk) p.kpos_ws[(int64_t)b * p.Sk + j] = j - K.lower(K.at(j));
-  }
-  if (bx >= p.n_qt) return;  // uniform per block
-  const int i = bx * bm + t;
-  if (t < bm && i < p.Sq) {
-    const int id = Q.at(i);
-    int lo = 0, hi = 0;
-    if (id >= 0) {
-      lo = K.lower(id);
-      hi = K.upper(id);
-    }
-    p.q_range[(int64_t)b * p.Sq + i] = make_int2(lo, hi);
-    if (p.qpos_ws) p.qpos_ws[(int64_t)b * p.Sq + i] = i - Q.lower(id);
-    if (hi > lo) {
-      atomicMin(&s_min_lo, lo);
-      atomicMax(&s_max_hi, hi);
-    }
-    atomicMax(&s_max_lo, hi > lo ? lo : 0);
-    atomicMin(&s_min_hi, hi > lo ? hi : 0);
-  }
+  if (k_lds && same) seg_prep_body(p, bm, bx, b, sk_l, sk_l, red);
+  else if (k_lds && q_lds) seg_prep_body(p, bm, bx, b, sk_l, sq_l, red);
+  else if (k_lds) seg_prep_body(p, bm, bx, b, sk_l, sq, red);
+  else if (same) seg_prep_body(p, bm, bx, b, sk, sk, red);
+  else if (q_lds) seg_prep_body(p, bm, bx, b, sk, sq_l, red);
+  else seg_prep_body(p, bm, bx, b, sk, sq, red);
   __syncthreads();
-  if (t == 0) {
+  if (t == 0 && bx < p.n_qt) {
     int4 r;
-    if (s_max_hi == INT_MIN) {  // no query of the tile has a live key
+    if (red[1] == INT_MIN) {  // no query of the tile has a live key
       r = make_int4(0, 0, 0, 0);
     } else {
-      r.x = s_min_lo / FWD_BN;
-      r.y = (s_max_hi + FWD_BN - 1) / FWD_BN;
-      r.z = (s_max_lo + FWD_BN - 1) / FWD_BN;
-      r.w = s_min_hi / FWD_BN;
+      r.x = red[0] / FWD_BN;
+      r.y = (red[1] + FWD_BN - 1) / FWD_BN;
+      r.z = (red[2] + FWD_BN - 1) / FWD_BN;
+      r.w = red[3] / FWD_BN;
       if (r.w < r.z) r.w = r.z;
     }
     p.qt_range[(int64_t)b * p.n_qt + bx] = r;

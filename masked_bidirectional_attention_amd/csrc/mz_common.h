@@ -119,21 +119,26 @@ __device__ inline float half_swap_sum(float x) {
 }
 
 // ---- rotary embedding angles -----------------------------------------------
-// Angle of pair i at position p is p * base^(-2i/D), evaluated in fp64 and
-// rounded to fp32 cos / sin at the end.  The angle is first reduced to
-// [-pi, pi] by subtracting the nearest multiple of 2*pi (2*pi split in two
-// doubles, Cody-Waite), so the fp64 sine / cosine only see small arguments.
-// The table holds positions [0, tab_len); other positions take the same
-// formula directly, so both routes give identical bits.
-__device__ inline float2 rope_cs_direct(int pos, int i, int D, double log2_base) {
-  const double theta = exp2(-(double)(2 * i) / (double)D * log2_base);
+// theta_i = base^(-2i/D) in fp64.  The angle pos * theta_i is formed in fp64
+// and reduced to [-pi, pi] by subtracting the nearest multiple of 2 pi (2 pi
+// split in two doubles, Cody-Waite), then its sine and cosine are taken in
+// fp32 (accurate to about one fp32 ulp on the reduced range).  The table
+// holds positions [0, tab_len); other positions take the same formula
+// directly, so both routes give identical bits.
+__device__ inline double rope_theta(int i, int D, double log2_base) {
+  return exp2(-(double)(2 * i) / (double)D * log2_base);
+}
+__device__ inline float2 rope_cs_theta(int pos, double theta) {
   const double ang = (double)pos * theta;
   const double k = rint(ang * 0.15915494309189533577);  // 1 / (2 pi)
   double r = fma(-k, 6.28318530717958623200, ang);     // 2 pi, high part
   r = fma(-k, 2.44929359829470635445e-16, r);           // 2 pi, low part
-  double s, c;
-  sincos(r, &s, &c);
-  return make_float2((float)c, (float)s);
+  float s, c;
+  sincosf((float)r, &s, &c);
+  return make_float2(c, s);
+}
+__device__ inline float2 rope_cs_direct(int pos, int i, int D, double log2_base) {
+  return rope_cs_theta(pos, rope_theta(i, D, log2_base));
 }
 
 __device__ inline float2 rope_cs(const float2* tab, int tab_len, int pos, int i, int D,

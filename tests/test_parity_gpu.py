@@ -255,3 +255,18 @@ def test_long_segment_rows_fwd(S):
     o = run_fwd(case)
     ref, _ = oracle_fwd(case)
     assert_parity("bf16", o, ref, f"long segments S={S}")
+
+
+def test_decode_call_set_cache():
+    import masked_bidirectional_attention_amd as mz
+    a = W.random_decode(32, 2, 8, 2, 1, 500, 128, "bf16", 400, 500)
+    b2 = W.random_decode(33, 2, 8, 2, 1, 500, 128, "bf16", 450, 500)
+    call = mz.DecodeCall(dev(a.q), dev(a.k_cache), dev(a.v_cache), span=500, mask=dev(a.mask))
+    o1 = call().clone()
+    call.set_cache(dev(b2.k_cache), dev(b2.v_cache))
+    o2 = call().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, run_decode(a))
+    ref = mzref.mzref_decode("bf16", W.to_bits(a.q), W.to_bits(b2.k_cache), W.to_bits(b2.v_cache), span=500,
+                             mask=a.mask.numpy())
+    assert_parity("bf16", o2, ref, "decode after set_cache")
