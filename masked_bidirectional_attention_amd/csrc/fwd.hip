@@ -401,44 +401,45 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
 
   // ---- direct-to-LDS tile loads.  Slot q of a padded tile is row q / KCH,
   // chunk q % KCH; pad slots (chunk >= CH) load chunk 0 of their row again.
-  // The per-lane element offsets within a tile are fixed (row strides are
-  // below 2^24 elements, so they fit 32 bits); only the last tile, whose
-  // rows past Sk load row Sk - 1 instead (their keys are masked), needs
-  // them recomputed.
-  uint32_t koff[KPW], voff[KPW > VPW ? KPW : VPW];
+  // The per-lane byte offsets from the tile's first row are fixed (row
+  // strides are below 2^24 elements, so a 64-row tile spans less than 2^31
+  // bytes); only the last tile, whose rows past Sk load row Sk - 1 instead
+  // (their keys are masked), needs them recomputed.
+  uint32_t koff[KPW], voff[VPW];
   auto slot_off = [&](int ins, int nch, int64_t stride, int key0, bool clamp) -> uint32_t {
     const int q = ins * 64 + lane;
     int row = q / nch;
     if (clamp) row = min(key0 + row, p.Sk - 1) - key0;
     const int ch = q % nch;
-    return (uint32_t)(row * stride + (ch < CH ? ch : 0) * 8);
+    return (uint32_t)((row * stride + (ch < CH ? ch : 0) * 8) * 2);
   };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave, KCH, kstride, 0, false);
+  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride, 0, false);
 #pragma unroll
-  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave, VCH, vstride, 0, false);
+  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave_u, VCH, vstride, 0, false);
+  const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
   auto load_kv = [&](int kt, int stage) {
     const int key0 = kt * BN;
     const uint16_t* ktb = kbase + (int64_t)key0 * kstride;
     const uint16_t* vtb = vbase + (int64_t)key0 * vstride;
-    uint16_t* kdst = &Ks[stage][0];
-    uint16_t* vdst = &Vs[stage][0];
+    const uint32_t kdst = ks_lds + stage * (BN * KS * 2), vdst = vs_lds + stage * (BN * VS * 2);
     if (key0 + BN <= p.Sk) {
 #pragma unroll
       for (int u = 0; u < KPW; ++u)
-        if (u * 4 + wave < KINS) lds_dma16(ktb + koff[u], kdst + (u * 4 + wave) * 512);
+        if (u * 4 + wave_u < KINS) lds_dma16_s(ktb, koff[u], kdst + (u * 4 + wave_u) * 1024);
 #pragma unroll
       for (int u = 0; u < VPW; ++u)
-        if (u * 4 + wave < VINS) lds_dma16(vtb + voff[u], vdst + (u * 4 + wave) * 512);
+        if (u * 4 + wave_u < VINS) lds_dma16_s(vtb, voff[u], vdst + (u * 4 + wave_u) * 1024);
     } else {
 #pragma unroll
       for (int u = 0; u < KPW; ++u)
-        if (u * 4 + wave < KINS)
-          lds_dma16(ktb + slot_off(u * 4 + wave, KCH, kstride, key0, true), kdst + (u * 4 + wave) * 512);
+        if (u * 4 + wave_u < KINS)
+          lds_dma16_s(ktb, slot_off(u * 4 + wave_u, KCH, kstride, key0, true), kdst + (u * 4 + wave_u) * 1024);
 #pragma unroll
       for (int u = 0; u < VPW; ++u)
-        if (u * 4 + wave < VINS)
-          lds_dma16(vtb + slot_off(u * 4 + wave, VCH, vstride, key0, true), vdst + (u * 4 + wave) * 512);
+        if (u * 4 + wave_u < VINS)
+          lds_dma16_s(vtb, slot_off(u * 4 + wave_u, VCH, vstride, key0, true), vdst + (u * 4 + wave_u) * 1024);
     }
   };
 
@@ -454,6 +455,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
       }
     }
   };
+
+  // every prologue load completes here, so that no wait for it is left
+  // inside the tile loop (where it would also wait for the tile copies)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) __asm__ volatile("" ::"v"(qf[s].x), "v"(qf[s].y), "v"(qf[s].z), "v"(qf[s].w));
+  __asm__ volatile("" ::"v"(lo), "v"(hi));
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[ND];

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace mz {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -37,6 +40,11 @@ template <> struct Elem<BF16> {
     const f32x2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
+  // acc + both halves of a packed pair (one v_dot2 with (1, 1))
+  __device__ static inline float add_pair(uint32_t x, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), one, acc, false);
+  }
 };
 template <> struct Elem<F16> {
   __device__ static inline float to_f32(uint16_t b) {
@@ -50,6 +58,11 @@ template <> struct Elem<F16> {
   __device__ static inline uint32_t pack2(float a, float b) {
     const f32x2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  // acc + both halves of a packed pair (one v_dot2 with (1, 1))
+  __device__ static inline float add_pair(uint32_t x, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), one, acc, false);
   }
 };
 
@@ -98,6 +111,28 @@ template <> __device__ inline uint2 lds_read_tr<F16>(const uint16_t* p) {
 // wave writes its 16 bytes to lds_base + 16 * i (lds_base is wave-uniform).
 __device__ inline void lds_dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// 16-byte global -> LDS copy: lane i reads bytes [voff_i, voff_i + 16) past
+// the wave-uniform base and writes them to LDS byte address lds_addr + 16*i
+// (lds_addr is wave-uniform; it goes to M0, and the s_nop gives the M0
+// write the wait state the LDS-DMA path needs).  Issued as opaque assembly
+// on purpose: the compiler then cannot see the LDS write and does not make
+// the following LDS reads of the other pipeline stage wait for it; the
+// caller waits with "s_waitcnt vmcnt(0)" and a barrier before reading the
+// stage it fills.
+__device__ inline void lds_dma16_s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  // the base is wave-uniform by contract; make it scalar explicitly
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs),
+                   "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr))
+                   : "memory");
+}
+// LDS byte address of a pointer into shared memory
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const MZ_LDS void*)p;
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -167,6 +202,17 @@ __device__ inline uint4 rope_quad(uint4 x, const float2* tab, int tab_len, int p
 
 // Map a hardware block id to a work item so that consecutive work items land
 // on one XCD (blocks are dispatched round-robin over the 8 XCDs).
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... up to N - 1,
+// each body a separate straight-line copy (no reliance on the unroller).
+template <typename F, int... Us>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, Us...>) {
+  (f(std::integral_constant<int, Us>{}), ...);
+}
+template <int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ inline int xcd_remap(int bid, int n) {
   const int n8 = n - (n & 7);
   if (bid >= n8) return bid;
