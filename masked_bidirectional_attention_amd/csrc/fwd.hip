@@ -406,53 +406,52 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   // bytes); only the last tile, whose rows past Sk load row Sk - 1 instead
   // (their keys are masked), needs them recomputed.
   uint32_t koff[KPW], voff[VPW];
-  auto slot_off = [&](int ins, int nch, int64_t stride, int key0, bool clamp) -> uint32_t {
+  auto slot_off = [&](int ins, int nch, int64_t stride) -> uint32_t {
     const int q = ins * 64 + lane;
-    int row = q / nch;
-    if (clamp) row = min(key0 + row, p.Sk - 1) - key0;
+    const int row = q / nch;
     const int ch = q % nch;
     return (uint32_t)((row * stride + (ch < CH ? ch : 0) * 8) * 2);
   };
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride, 0, false);
+  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride);
 #pragma unroll
-  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave_u, VCH, vstride, 0, false);
+  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave_u, VCH, vstride);
   const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
-  auto load_kv = [&](int kt, int stage) {
+  // descriptor of one K or V tile: its rows below Sk only, so rows past Sk
+  // read as zeros (their keys are masked)
+  auto tile_desc = [&](const uint16_t* base, int64_t stride, int kt) -> u32x4_t {
     const int key0 = kt * BN;
-    const uint16_t* ktb = kbase + (int64_t)key0 * kstride;
-    const uint16_t* vtb = vbase + (int64_t)key0 * vstride;
-    const uint32_t kdst = ks_lds + stage * (BN * KS * 2), vdst = vs_lds + stage * (BN * VS * 2);
-    if (key0 + BN <= p.Sk) {
-#pragma unroll
-      for (int u = 0; u < KPW; ++u)
-        if (u * 4 + wave_u < KINS) lds_dma16_s(ktb, koff[u], kdst + (u * 4 + wave_u) * 1024);
-#pragma unroll
-      for (int u = 0; u < VPW; ++u)
-        if (u * 4 + wave_u < VINS) lds_dma16_s(vtb, voff[u], vdst + (u * 4 + wave_u) * 1024);
-    } else {
-#pragma unroll
-      for (int u = 0; u < KPW; ++u)
-        if (u * 4 + wave_u < KINS)
-          lds_dma16_s(ktb, slot_off(u * 4 + wave_u, KCH, kstride, key0, true), kdst + (u * 4 + wave_u) * 1024);
-#pragma unroll
-      for (int u = 0; u < VPW; ++u)
-        if (u * 4 + wave_u < VINS)
-          lds_dma16_s(vtb, slot_off(u * 4 + wave_u, VCH, vstride, key0, true), vdst + (u * 4 + wave_u) * 1024);
-    }
+    const int rows = min(BN, p.Sk - key0);
+    return buf_desc(base + (int64_t)key0 * stride, (uint32_t)(((int64_t)(rows - 1) * stride + D) * 2));
   };
-
-  // ---- S^T = K Q^T + cinit of one tile (log2 domain)
-  auto qk = [&](int stage, f32x16_t (&sacc)[2], const f32x16_t& c0) {
+  auto load_k = [&](int kt, int stage) {
+    const u32x4_t d = tile_desc(kbase, kstride, kt);
+    const uint32_t kdst = ks_lds + stage * (BN * KS * 2);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int u = 0; u < KPW; ++u)
+      if (u * 4 + wave_u < KINS) lds_dma16_b(d, koff[u], kdst + (u * 4 + wave_u) * 1024);
+  };
+  auto load_v = [&](int kt, int stage) {
+    const u32x4_t d = tile_desc(vbase, vstride, kt);
+    const uint32_t vdst = vs_lds + stage * (BN * VS * 2);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + l32;
-        const uint4 a = *(const uint4*)&Ks[stage][row * KS + (2 * s + hh) * 8];
-        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? c0 : sacc[kb]);
-      }
+    for (int u = 0; u < VPW; ++u)
+      if (u * 4 + wave_u < VINS) lds_dma16_b(d, voff[u], vdst + (u * 4 + wave_u) * 1024);
+  };
+  // the copies of one step spread over its MFMA slots: slot u < KPW is K
+  // copy instruction u of this wave, slot KPW + u V copy u
+  struct DmaPlan {
+    u32x4_t dk, dv;
+    uint32_t kdst, vdst;
+    bool k_on, v_on;
+  };
+  auto dma_slot = [&](const DmaPlan& pl, int slot) {
+    if (slot < KPW) {
+      if (pl.k_on && slot * 4 + wave_u < KINS) lds_dma16_b(pl.dk, koff[slot], pl.kdst + (slot * 4 + wave_u) * 1024);
+    } else {
+      const int u = slot - KPW;
+      if (pl.v_on && u * 4 + wave_u < VINS) lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
     }
   };
 
@@ -468,95 +467,88 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-
   const int grp = lane >> 4, gi = lane & 15, rr = gi >> 2, cc = gi & 3;
 
-  // Pipeline: tile j's K and V sit in stage j % 2 while tile j + 1's K and V
-  // stream into the other stage.  One barrier per tile: after it, every
-  // wave is done with tile j - 1 (the stage the next loads overwrite) and
-  // tile j has landed.
-  int kt = next_live(kt_beg);
-  if (kt < kt_end) load_kv(kt, 0);
-  int j = 0;
-  // scores come out of the MFMA already shifted by -m (the accumulator
-  // starts at -m instead of 0); cinit changes only when m does
-  f32x16_t cinit = {};
-  while (kt < kt_end) {
-    const int stage = __builtin_amdgcn_readfirstlane(j & 1);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int kt1 = next_live(kt + 1);
-    if (kt1 < kt_end) load_kv(kt1, stage ^ 1);
-    f32x16_t scur[2];
-    qk(stage, scur, cinit);
+  const f32x16_t zero16 = {};
+  f32x16_t scur[2], snext[2];
+  float mu = 0.f;  // reference of the exponentials (m, or 0 before any live key)
 
-    // ---- remove non-live keys (boundary tiles only)
+  // S^T = K Q^T + cinit of one tile, plain (prologue)
+  auto qk = [&](int stage, f32x16_t (&sacc)[2]) {
+    const uint16_t* kt_lds = &Ks[stage][0];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 a = *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * s + hh) * 8];
+        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? zero16 : sacc[kb]);
+      }
+    }
+  };
+  // non-live keys of a boundary tile -> -inf.  Key kb*32 + c + hh*4 of the
+  // tile (c a compile-time constant per register) is compared through
+  // per-tile thresholds, so no per-register key offset stays in registers.
+  auto mask_tile = [&](int kt, f32x16_t (&sc)[2]) {
     bool check;
     if constexpr (MK == 2) check = !(kt >= full_beg && kt < full_end);
     else if constexpr (MK == 1) check = cls_at(kt) == 2 || kt >= first_tail_tile;
     else check = kt >= first_tail_tile;
-    if (check) {
+    if (__builtin_expect(check, 0)) {
+      // kept a branch (boundary tiles are few): without the barrier to
+      // speculation the compiler turns this into selects on every tile
+      __asm__ volatile("");
+      const int base = kt * BN + hh * 4;
+      const int lim = p.Sk - base;       // keys past Sk
+      const int lo_t = lo - base, hi_t = hi - base;
+      const uint8_t* mb = mrow != nullptr ? mrow + base : nullptr;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = kt * BN + kb * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+          const int c = kb * 32 + (v >> 2) * 8 + (v & 3);
           bool live;
-          if constexpr (MK == 2) live = key >= lo && key < hi;
-          else if constexpr (MK == 1) live = key < p.Sk && mrow != nullptr && mrow[key] != 0;
-          else live = key < p.Sk;
-          scur[kb][v] = live ? scur[kb][v] : -INFINITY;
+          if constexpr (MK == 2) live = c >= lo_t && c < hi_t;
+          else if constexpr (MK == 1) live = c < lim && mb != nullptr && mb[c] != 0;
+          else live = c < lim;
+          sc[kb][v] = live ? sc[kb][v] : -INFINITY;
         }
       }
     }
-
-    // ---- online softmax with lazy rescaling.  scur holds s - m_use, where
-    // m_use is the running reference (0 before any live key).  The reference
-    // moves only when a score exceeds it by more than 2^8.
+  };
+  auto rowmax = [&](const f32x16_t (&sc)[2]) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, scur[kb][v]), scur[kb][v + 1]);
-    mx = half_swap_max(mx);
-    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx > LAZY_RESCALE_LOG2;
-    if (__any(need)) {
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      const float delta = need ? mx : 0.f;
-      const float m_new = need ? m_use + delta : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) scur[kb][v] -= delta;
-      const float nm = m_run == -INFINITY ? 0.f : -m_run;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) cinit[v] = nm;
-    }
-    uint4 pk[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e]);
-          const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1]);
-          l_run += p0 + p1;
-          wv[e] = Elem<T>::pack2(p0, p1);
-        }
-        pk[kb][jj] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
-    }
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, sc[kb][v]), sc[kb][v + 1]);
+    return half_swap_max(mx);
+  };
 
-    // ---- O^T += V^T P^T
+  // Software pipeline over the live key tiles t(0), t(1), ...  During step
+  // j, K of t(j+1) and V of t(j) are resident (K one tile ahead of V) while
+  // K of t(j+2) and V of t(j+1) stream in; one barrier per step.  LDS
+  // operands are read PF MFMAs ahead of their use; a scheduling fence after
+  // each MFMA keeps the planned order.
+  constexpr int PF = 2;
+  uint4 pk[2][2];
+  float mx_next = -INFINITY;
+  constexpr int NSLOT = KPW + VPW;  // copy instructions per wave and step, at most
+  // the last tile: its exponentials, then its P.V
+  auto last_tile = [&](int vstage) {
+    float lsa = 0.f, lsb = 0.f;
+    uint32_t wv[2][2][4];
+    static_for<16>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
+      const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - mu);
+      const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - mu);
+      wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
+      if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
+      else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
+      if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
+    });
+    l_run += lsa + lsb;
+    const uint16_t* vt_lds = &Vs[vstage][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -565,14 +557,152 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
         for (int db = 0; db < ND; ++db) {
           const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
           const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
-          const uint2 a0 = lds_read_tr<T>(&Vs[stage][r0 * VS + col]);
-          const uint2 a1 = lds_read_tr<T>(&Vs[stage][(r0 + 8) * VS + col]);
+          const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
+          const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
           oacc[db] = mfma32<T>(make_uint4(a0.x, a0.y, a1.x, a1.y), pk[kb][jj], oacc[db]);
         }
       }
     }
-    kt = kt1;
-    ++j;
+  };
+
+  // Steady-state step, merged: the 2*NS MFMAs of K Q^T for t(j+1) (two
+  // accumulator chains) alternate with the 4*ND MFMAs of P.V for t(j) (ND
+  // chains), so consecutive MFMAs of one chain sit several slots apart and
+  // no MFMA waits on the latency of its predecessor.  P block (kb, jj) is
+  // produced by exponential pieces in the slots before the first P.V MFMA
+  // that reads it; the copies of the step take odd slots.
+  constexpr int NQK = 2 * NS, NPV = 4 * ND;
+  static_assert(NQK == NPV, "alternating schedule");
+  auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4]) {
+    constexpr int h = decltype(hc)::value;
+    constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
+    const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - mu);
+    const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - mu);
+    wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
+    __asm__ volatile("" ::"v"(wv[kb][jj][e]));
+    if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
+    else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
+    if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
+  };
+  auto step_merged = [&](int kstage, int vstage, const DmaPlan& pl) {
+    const uint16_t* kt_lds = &Ks[kstage][0];
+    const uint16_t* vt_lds = &Vs[vstage][0];
+    float lsa = 0.f, lsb = 0.f;
+    uint32_t wv[2][2][4];
+    // P block (0, 0) before the first P.V MFMA
+    static_for<4>([&](auto hc) { exp_piece(hc, lsa, lsb, wv); });
+    auto kfrag = [&](auto gc) -> uint4 {
+      constexpr int g = decltype(gc)::value, ss = g >> 1, kb = g & 1;
+      return *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * ss + hh) * 8];
+    };
+    auto vfrag = [&](auto gc) -> uint4 {
+      constexpr int g = decltype(gc)::value, kb = g / (2 * ND), jj = (g / ND) & 1, db = g % ND;
+      const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
+      const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
+      const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
+      const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
+      return make_uint4(a0.x, a0.y, a1.x, a1.y);
+    };
+    uint4 frk[PF], frv[PF];
+    static_for<PF>([&](auto gc) {
+      frk[decltype(gc)::value] = kfrag(gc);
+      frv[decltype(gc)::value] = vfrag(gc);
+    });
+    // slot 2i: K Q^T MFMA i; slot 2i+1: P.V MFMA i
+    static_for<2 * NQK>([&](auto uc) {
+      constexpr int u = decltype(uc)::value, i = u >> 1;
+      if constexpr ((u & 1) == 0) {
+        constexpr int ss = i >> 1, kb = i & 1;
+        const uint4 f = frk[i % PF];
+        if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
+        snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? zero16 : snext[kb]);
+        // exponential pieces of P blocks (0,1), (1,0), (1,1): piece h in
+        // slot 2 * (h - 4) * NQK / 12 + 2, before the P.V MFMAs reading it
+        static_for<16>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          if constexpr (h >= 4 && 2 * ((h - 4) * (NQK - 2) / 12) == u) exp_piece(hc, lsa, lsb, wv);
+        });
+      } else {
+        constexpr int kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
+        const uint4 f = frv[i % PF];
+        if constexpr (i + PF < NPV) frv[i % PF] = vfrag(std::integral_constant<int, i + PF>{});
+        oacc[db] = mfma32<T>(f, pk[kb][jj], oacc[db]);
+        if constexpr (i >= 1 && i - 1 < NSLOT) dma_slot(pl, i - 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    l_run += lsa + lsb;
+  };
+
+  int kt = next_live(kt_beg);
+  int kn = kt < kt_end ? next_live(kt + 1) : kt_end;
+  if (kt < kt_end) {
+    load_k(kt, 0);
+    load_v(kt, 0);
+  }
+  if (kn < kt_end) load_k(kn, 1);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  float mx = -INFINITY;
+  if (kt < kt_end) {
+    qk(0, scur);
+    mask_tile(kt, scur);
+    mx = rowmax(scur);
+  }
+  // one step: rescale for t(j) if needed, then [K Q^T of t(j+1)] with the
+  // exponentials of t(j), then P.V of t(j) [with the row max of t(j+1)]
+  auto rescale_step = [&]() {
+    // ---- online softmax with lazy rescaling.  The reference m of a query
+    // moves only when a score exceeds it by more than 2^8 (otherwise the
+    // exponentials stay below 256); numerator and denominator always share
+    // it, so the result is the same softmax.
+    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx > m_run + LAZY_RESCALE_LOG2;
+    if (__any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      mu = m_run == -INFINITY ? 0.f : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    }
+  };
+  auto step_top = [&](int j) {
+    // K of t(j+1) and V of t(j) have landed once this barrier passes, and
+    // every wave is done with the stages the next copies overwrite
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  int j = 0;
+  if (kt < kt_end) {
+    while (kn < kt_end) {
+      step_top(j);
+      const int kn2 = next_live(kn + 1);
+      // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
+      DmaPlan pl;
+      pl.k_on = kn2 < kt_end;
+      pl.dk = tile_desc(kbase, kstride, pl.k_on ? kn2 : kn);
+      pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
+      pl.v_on = true;
+      pl.dv = tile_desc(vbase, vstride, kn);
+      pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
+      rescale_step();
+      step_merged((j + 1) & 1, j & 1, pl);
+      mask_tile(kn, snext);
+      mx_next = rowmax(snext);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
+      mx = mx_next;
+      kt = kn;
+      kn = kn2;
+      ++j;
+    }
+    // the last tile
+    step_top(j);
+    rescale_step();
+    last_tile(j & 1);
   }
 
   // ---- epilogue: O = O^T / l, lse

@@ -130,6 +130,26 @@ __device__ inline void lds_dma16_s(const void* base, uint32_t voff, uint32_t lds
                    "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr))
                    : "memory");
 }
+// Raw buffer descriptor (stride 0, 32-bit data format) over nbytes bytes
+// from a wave-uniform base, in scalar registers: a load whose bytes lie past
+// nbytes returns zeros instead.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x4_t buf_desc(const void* base, uint32_t nbytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  u32x4_t d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu;
+  d.z = __builtin_amdgcn_readfirstlane(nbytes);
+  d.w = 0x00020000u;
+  return d;
+}
+// The same copy through a buffer descriptor (range-checked, see buf_desc).
+__device__ inline void lds_dma16_b(u32x4_t desc, uint32_t voff, uint32_t lds_addr) {
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
+                   "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr))
+                   : "memory");
+}
+
 // LDS byte address of a pointer into shared memory
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const MZ_LDS void*)p;
