@@ -470,7 +470,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   const int grp = lane >> 4, gi = lane & 15, rr = gi >> 2, cc = gi & 3;
 
   const f32x16_t zero16 = {};
-  f32x16_t scur[2], snext[2];
+  // scores of two consecutive tiles; the steady-state loop is unrolled by
+  // two so that the arrays swap roles instead of being copied
+  f32x16_t sA[2], sB[2];
   float mu = 0.f;  // reference of the exponentials (m, or 0 before any live key)
 
   // S^T = K Q^T + cinit of one tile, plain (prologue)
@@ -531,10 +533,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   // each MFMA keeps the planned order.
   constexpr int PF = 2;
   uint4 pk[2][2];
-  float mx_next = -INFINITY;
   constexpr int NSLOT = KPW + VPW;  // copy instructions per wave and step, at most
   // the last tile: its exponentials, then its P.V
-  auto last_tile = [&](int vstage) {
+  auto last_tile = [&](int vstage, f32x16_t (&scur)[2]) {
     float lsa = 0.f, lsb = 0.f;
     uint32_t wv[2][2][4];
     static_for<16>([&](auto hc) {
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   // that reads it; the copies of the step take odd slots.
   constexpr int NQK = 2 * NS, NPV = 4 * ND;
   static_assert(NQK == NPV, "alternating schedule");
-  auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4]) {
+  auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4], f32x16_t (&scur)[2]) {
     constexpr int h = decltype(hc)::value;
     constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
     const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - mu);
@@ -584,13 +585,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
     else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
     if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
   };
-  auto step_merged = [&](int kstage, int vstage, const DmaPlan& pl) {
+  auto step_merged = [&](int kstage, int vstage, const DmaPlan& pl, f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
     const uint16_t* kt_lds = &Ks[kstage][0];
     const uint16_t* vt_lds = &Vs[vstage][0];
     float lsa = 0.f, lsb = 0.f;
     uint32_t wv[2][2][4];
     // P block (0, 0) before the first P.V MFMA
-    static_for<4>([&](auto hc) { exp_piece(hc, lsa, lsb, wv); });
+    static_for<4>([&](auto hc) { exp_piece(hc, lsa, lsb, wv, scur); });
     auto kfrag = [&](auto gc) -> uint4 {
       constexpr int g = decltype(gc)::value, ss = g >> 1, kb = g & 1;
       return *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * ss + hh) * 8];
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
         // slot 2 * (h - 4) * NQK / 12 + 2, before the P.V MFMAs reading it
         static_for<16>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
-          if constexpr (h >= 4 && 2 * ((h - 4) * (NQK - 2) / 12) == u) exp_piece(hc, lsa, lsb, wv);
+          if constexpr (h >= 4 && 2 * ((h - 4) * (NQK - 2) / 12) == u) exp_piece(hc, lsa, lsb, wv, scur);
         });
       } else {
         constexpr int kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
@@ -645,9 +646,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
   __syncthreads();
   float mx = -INFINITY;
   if (kt < kt_end) {
-    qk(0, scur);
-    mask_tile(kt, scur);
-    mx = rowmax(scur);
+    qk(0, sA);
+    mask_tile(kt, sA);
+    mx = rowmax(sA);
   }
   // one step: rescale for t(j) if needed, then [K Q^T of t(j+1)] with the
   // exponentials of t(j), then P.V of t(j) [with the row max of t(j+1)]
@@ -676,33 +677,41 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(const FwdParams p) {
     __syncthreads();
   };
   int j = 0;
+  // one steady-state step: tile t(j) scores in sc, t(j+1) scores into sn
+  auto steady = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    step_top(j);
+    const int kn2 = next_live(kn + 1);
+    // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
+    DmaPlan pl;
+    pl.k_on = kn2 < kt_end;
+    pl.dk = tile_desc(kbase, kstride, pl.k_on ? kn2 : kn);
+    pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
+    pl.v_on = true;
+    pl.dv = tile_desc(vbase, vstride, kn);
+    pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
+    rescale_step();
+    step_merged((j + 1) & 1, j & 1, pl, sc, sn);
+    mask_tile(kn, sn);
+    mx = rowmax(sn);
+    kt = kn;
+    kn = kn2;
+    ++j;
+  };
   if (kt < kt_end) {
+    bool in_b = false;  // the current tile's scores are in sB
     while (kn < kt_end) {
-      step_top(j);
-      const int kn2 = next_live(kn + 1);
-      // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
-      DmaPlan pl;
-      pl.k_on = kn2 < kt_end;
-      pl.dk = tile_desc(kbase, kstride, pl.k_on ? kn2 : kn);
-      pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
-      pl.v_on = true;
-      pl.dv = tile_desc(vbase, vstride, kn);
-      pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
-      rescale_step();
-      step_merged((j + 1) & 1, j & 1, pl);
-      mask_tile(kn, snext);
-      mx_next = rowmax(snext);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
-      mx = mx_next;
-      kt = kn;
-      kn = kn2;
-      ++j;
+      steady(sA, sB);
+      if (kn >= kt_end) {
+        in_b = true;
+        break;
+      }
+      steady(sB, sA);
     }
     // the last tile
     step_top(j);
     rescale_step();
-    last_tile(j & 1);
+    if (in_b) last_tile(j & 1, sB);
+    else last_tile(j & 1, sA);
   }
 
   // ---- epilogue: O = O^T / l, lse
