@@ -87,18 +87,22 @@ __device__ inline void fold_into(Part2& x, float m, float l, float a0, float a1)
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one work-group per (batch, kv-head, row).  The fold order
-// is fixed by chunk index alone: chunks are taken in super-groups of 64;
-// within one, group g of threads folds chunks [g*CG, (g+1)*CG) in order,
-// then the group partials are folded in g order, then super-groups in
-// order.  Chunks at or past n_chunks are identities, so the result does
-// not depend on how many chunks the span covered beyond its live keys.
+// Merge kernel: one work-group per (batch, kv-head, row).  Chunks are taken
+// in super-groups of 64; within one, thread group g holds chunks
+// [g*CG, (g+1)*CG) of it.  The super-group's maximum m over its live chunks
+// (l > 0) is exact; every live chunk then contributes its l and acc scaled
+// by 2^(m_c - m), summed in chunk order within a group and in group order
+// across groups; super-groups are folded in order.  Chunks at or past
+// n_chunks contribute exact zeros and a super-group without live chunks is
+// the identity of the fold, so the result does not depend on how many
+// chunks the span covered beyond its live keys.
 // ---------------------------------------------------------------------------
 template <int D, typename Store>
 __device__ void decode_merge_row(const DecodeParams& p, Store store) {
   constexpr int HD = D / 2;     // d pairs
   constexpr int NG = 256 / HD;  // chunk groups (4 for D 128, 8 for D 64)
   constexpr int CG = 64 / NG;   // chunks per group per super-group
+  __shared__ float gmax[NG];
   __shared__ Part2 red[256];
   const int row = blockIdx.x;  // (unit, n)
   const int n = row % p.R, unit = row / p.R;
@@ -109,7 +113,7 @@ __device__ void decode_merge_row(const DecodeParams& p, Store store) {
   Part2 tot = {0.f, 0.f, 0.f, 0.f};
   for (int sg = 0; sg * 64 < p.n_chunks; ++sg) {
     const int c0 = sg * 64 + g * CG;
-    // every load of the group first, then the fold
+    // every load of the group first
     float2 mc[CG], ac[CG];
 #pragma unroll
     for (int i = 0; i < CG; ++i) {
@@ -121,9 +125,23 @@ __device__ void decode_merge_row(const DecodeParams& p, Store store) {
         ac[i] = *(const float2*)(pa + (int64_t)c * p.R * D);
       }
     }
-    Part2 x = {0.f, 0.f, 0.f, 0.f};
+    // exact maximum over the super-group's live chunks
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < CG; ++i) fold_into(x, mc[i].x, mc[i].y, ac[i].x, ac[i].y);
+    for (int i = 0; i < CG; ++i) mx = mc[i].y > 0.f ? fmaxf(mx, mc[i].x) : mx;
+    if (dp == 0) gmax[g] = mx;
+    __syncthreads();
+    float m = gmax[0];
+#pragma unroll
+    for (int gg = 1; gg < NG; ++gg) m = fmaxf(m, gmax[gg]);
+    Part2 x = {m, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CG; ++i) {
+      const float f = mc[i].y > 0.f ? fast_exp2(mc[i].x - m) : 0.f;
+      x.l = fmaf(mc[i].y, f, x.l);
+      x.a0 = fmaf(ac[i].x, f, x.a0);
+      x.a1 = fmaf(ac[i].y, f, x.a1);
+    }
     red[t] = x;
     __syncthreads();
     if (g == 0) {
@@ -131,7 +149,9 @@ __device__ void decode_merge_row(const DecodeParams& p, Store store) {
 #pragma unroll
       for (int gg = 1; gg < NG; ++gg) {
         const Part2 z = red[gg * HD + dp];
-        fold_into(y, z.m, z.l, z.a0, z.a1);
+        y.l += z.l;
+        y.a0 += z.a0;
+        y.a1 += z.a1;
       }
       fold_into(tot, y.m, y.l, y.a0, y.a1);
     }
@@ -305,30 +325,51 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
       oacc[nb][db] = mfma16<T>(a, pb[nb], z);
     }
   }
-  // fold the 4 waves in fixed order through LDS: acc_lds[n][d] (reuses the
-  // V region once every wave has finished reading it)
+  // fold the 4 waves in fixed order through LDS (reusing the V region once
+  // every wave has finished reading it) and write the chunk partial
   __syncthreads();
-  for (int step = 0; step < 4; ++step) {
-    if (wave == step) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int n = nb * 16 + l16;
-            const int d = db * 16 + g4 * 4 + v;
-            float* slot = &acc_lds[n * D + d];
-            *slot = step == 0 ? oacc[nb][db][v] : *slot + oacc[nb][db][v];
-          }
-    }
-    __syncthreads();
-  }
-  // ---- write the chunk partial
   const int64_t pbase = ((int64_t)unit * p.n_chunks + c) * p.R;
-  for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
-    const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
-    *(float4*)(p.part_acc + (pbase + n) * D + d) = *(const float4*)&acc_lds[n * D + d];
+  if constexpr (sizeof(float) * 4 * RP * D <= sizeof(uint16_t) * 4 * 32 * VSD) {
+    // every wave parks its block in its own region; then all threads add
+    // the four in wave order
+    float* const own = acc_lds + wave * (RP * D);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) own[(nb * 16 + l16) * D + db * 16 + g4 * 4 + v] = oacc[nb][db][v];
+    __syncthreads();
+    for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
+      const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
+      float4 x = *(const float4*)&acc_lds[n * D + d];
+#pragma unroll
+      for (int wv = 1; wv < 4; ++wv) {
+        const float4 y = *(const float4*)&acc_lds[wv * (RP * D) + n * D + d];
+        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      }
+      *(float4*)(p.part_acc + (pbase + n) * D + d) = x;
+    }
+  } else {
+    // larger row counts: one shared block, waves adding in turn
+    for (int step = 0; step < 4; ++step) {
+      if (wave == step) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float* slot = &acc_lds[(nb * 16 + l16) * D + db * 16 + g4 * 4 + v];
+              *slot = step == 0 ? oacc[nb][db][v] : *slot + oacc[nb][db][v];
+            }
+      }
+      __syncthreads();
+    }
+    for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
+      const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
+      *(float4*)(p.part_acc + (pbase + n) * D + d) = *(const float4*)&acc_lds[n * D + d];
+    }
   }
   for (int n = tid; n < p.R; n += 256) {
     const float m = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
