@@ -211,6 +211,25 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const uint16_t* kbase = (const uint16_t*)p.k + b * p.ks[0] + kvh * p.ks[1];
   const uint16_t* vbase = (const uint16_t*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
+  // ---- a chunk in which no (row, key) pair is live is the identity of the
+  // merge: found from the mask alone, its K/V are never read
+  if (p.mask != nullptr) {
+    const int ckey0 = c * DEC_CHUNK;
+    // rows that share mask bytes (broadcast over heads and queries) are
+    // scanned once
+    const int rows = (p.ms[1] == 0 && p.ms[2] == 0) ? 1 : p.R;
+    bool any = false;
+    for (int idx = tid; idx < rows * DEC_CHUNK; idx += 256)
+      any |= dec_live(p, b, kvh, idx / DEC_CHUNK, ckey0 + idx % DEC_CHUNK);
+    if (!__syncthreads_or(any)) {
+      const int64_t pb = ((int64_t)unit * p.n_chunks + c) * p.R;
+      for (int idx = tid; idx < p.R * (D / 4); idx += 256)
+        *(float4*)(p.part_acc + (pb + idx / (D / 4)) * D + (idx % (D / 4)) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int n = tid; n < p.R; n += 256) p.part_ml[pb + n] = make_float2(0.f, 0.f);
+      return;
+    }
+  }
+
   // ---- issue every global load of this wave up front
   uint4 kf[2][NS];
 #pragma unroll
