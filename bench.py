@@ -242,6 +242,34 @@ def main(argv=None):
 
     tflops = fwd_flops() / (fwd_ms * 1e-3) / 1e12
     gbs = decode_bytes() / (dec_ms * 1e-3) / 1e9
+
+    # ---- the decode step at other cache fills (reported, not the headline):
+    # the same cold cache copies under the mask of fill L, at the full span
+    # and at the span rounded up to 256
+    by_fill = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for L in (257, 1024, 3100):
+        mask_l = torch.zeros_like(dmask)
+        mask_l[..., :L] = True
+        for span in (8192, W.ceil256(L)):
+            dl = mz.DecodeCall(dq, kc0, vc0, span=span, mask=mask_l, scale=c4.scale)
+            n = 50
+            for i in range(5):
+                dl.set_cache(*copies[i % len(copies)])
+                dl()
+            torch.cuda.synchronize()
+            tot = 0.0
+            for i in range(n):
+                dl.set_cache(*copies[i % len(copies)])
+                e0.record()
+                dl()
+                e1.record()
+                torch.cuda.synchronize()
+                tot += e0.elapsed_time(e1)
+            us = tot / n * 1e3
+            by_fill.append({"fill": L, "span": span, "us": round(us, 2),
+                            "GB/s": round(decode_bytes(L, span) / (us * 1e-6) / 1e9, 1),
+                            "algorithmic_mb": round(decode_bytes(L, span) / 1e6, 3)})
     traffic = {}
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
@@ -295,6 +323,7 @@ def main(argv=None):
                 "kernel_us": round(dec_ms * 1e3, 2),
                 "algorithmic_mb": round(decode_bytes() / 1e6, 3),
             },
+            "by_fill": by_fill,
         },
         "device": props.name,
     }
