@@ -126,6 +126,40 @@ def test_random_fwd(dtype, shape, kind):
     np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=1e-4 if dtype == "f32" else 3e-2)
 
 
+KS_SHAPES = [
+    (1, 4, 2, 200, 256, 128),   # 4 key tiles: both streams take two
+    (2, 8, 1, 129, 300, 128),   # 5 key tiles: stream 1 takes one fewer
+    (1, 2, 2, 300, 129, 64),    # 3 key tiles, D 64
+    (1, 16, 2, 257, 513, 128),  # 9 key tiles, ragged tails on both axes
+]
+
+
+@pytest.mark.parametrize("streams", ["1", "2"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", KS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["none", "bool_blocky", "bool_key", "segment"])
+def test_key_streams(monkeypatch, streams, dtype, shape, kind):
+    """Both work-group shapes of the MFMA kernel (one key stream, or two
+    streams over alternate key tiles merged at the end) against the oracle,
+    with odd and even live tile counts and tile classes that skip tiles."""
+    monkeypatch.setenv("MZATTN_KEY_STREAMS", streams)
+    B, Hq, Hkv, Sq, Sk, D = shape
+    seed = zlib.crc32(repr(("ks", dtype, shape, kind)).encode()) % 10000
+    if kind == "segment":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sq, D, dtype, W.MASK_SEGMENT, rope_base=1e4, n_segments=3)
+    elif kind == "none":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_NONE, rope_base=1e4)
+    else:
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_BOOL,
+                            mask_shape={"bool_blocky": "blocky", "bool_key": "key"}[kind], rope_base=1e4)
+    o, lse = run_fwd(case, return_lse=True)
+    ref, lse_ref = oracle_fwd(case)
+    assert_parity(dtype, o, ref, f"{case.name} {shape} streams={streams}")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(to64(lse)), fin)
+    np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=3e-2)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_explicit_positions(dtype):
     case = W.random_fwd(11, 2, 4, 4, 100, 140, 64, dtype, W.MASK_NONE, rope_base=1e4, explicit_pos=True)
