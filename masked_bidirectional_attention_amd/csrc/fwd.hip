@@ -498,6 +498,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // two so that the arrays swap roles instead of being copied
   f32x16_t sA[2], sB[2];
   float mu = 0.f;  // reference of the exponentials (m, or 0 before any live key)
+  // CINIT (D 64): the K Q^T accumulators start from -mu in every element, so
+  // scores arrive relative to the reference and the exponentials need no
+  // subtraction.  At D 128 the 16 extra registers would spill; there the
+  // accumulators start from zero and mu is subtracted before each exponential.
+  constexpr bool CINIT = D == 64;
+  f32x16_t cinit = {};
 
   // S^T = K Q^T + cinit of one tile, plain (prologue)
   auto qk = [&](int stage, f32x16_t (&sacc)[2]) {
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint4 a = *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * s + hh) * 8];
-        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? zero16 : sacc[kb]);
+        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? (CINIT ? cinit : zero16) : sacc[kb]);
       }
     }
   };
@@ -583,8 +589,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     static_for<16>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
       constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
-      const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - mu);
-      const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - mu);
+      const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - (CINIT ? 0.f : mu));
+      const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - (CINIT ? 0.f : mu));
       wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
       if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
       else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
@@ -605,8 +611,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4], f32x16_t (&scur)[2]) {
     constexpr int h = decltype(hc)::value;
     constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
-    const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - mu);
-    const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - mu);
+    const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - (CINIT ? 0.f : mu));
+    const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - (CINIT ? 0.f : mu));
     wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
     __asm__ volatile("" ::"v"(wv[kb][jj][e]));
     if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         constexpr int ss = i >> 1, kb = i & 1;
         const uint4 f = frk[i % PF];
         if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
-        snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? zero16 : snext[kb]);
+        snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? (CINIT ? cinit : zero16) : snext[kb]);
         // exponential pieces of P blocks (0,1), (1,0), (1,1): piece h in
         // slot 2 * (h - 4) * NQK / 12 + 2, before the P.V MFMAs reading it
         static_for<16>([&](auto hc) {
@@ -682,22 +688,35 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   float mx = -INFINITY;
-  auto rescale_step = [&]() {
+  auto rescale_step = [&](f32x16_t (&sc)[2]) {
     // ---- online softmax with lazy rescaling.  The reference m of a query
     // moves only when a score exceeds it by more than 2^8 (otherwise the
     // exponentials stay below 256); numerator and denominator always share
-    // it, so the result is the same softmax.
-    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx > m_run + LAZY_RESCALE_LOG2;
+    // it, so the result is the same softmax.  With CINIT, scores and mx are
+    // relative to the current reference mu, and a move shifts the scores of
+    // the tile at hand and the start value of the next ones.
+    const float mx_abs = CINIT ? mu + mx : mx;
+    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx_abs > m_run + LAZY_RESCALE_LOG2;
     if (__any(need)) {
-      const float m_new = need ? mx : m_run;
+      const float m_new = need ? mx_abs : m_run;
       const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      const float mu_new = m_new == -INFINITY ? 0.f : m_new;
+      const float shift = mu - mu_new;
       m_run = m_new;
-      mu = m_run == -INFINITY ? 0.f : m_run;
+      mu = mu_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+      if constexpr (CINIT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[kb][v] += shift;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cinit[v] = -mu;
+      }
     }
   };
   auto step_top = [&](int j) {
@@ -724,7 +743,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     const int kn2 = advance(kn);
     // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
     const DmaPlan pl = plan_step(kn2);
-    rescale_step();
+    rescale_step(sc);
     step_merged((j + 1) & 1, j & 1, pl, sc, sn);
     mask_tile(kn, sn);
     mx = rowmax(sn);
@@ -747,9 +766,13 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     }
     // the last tile
     step_top(j);
-    rescale_step();
-    if (in_b) last_tile(j & 1, sB);
-    else last_tile(j & 1, sA);
+    if (in_b) {
+      rescale_step(sB);
+      last_tile(j & 1, sB);
+    } else {
+      rescale_step(sA);
+      last_tile(j & 1, sA);
+    }
   }
 
   if constexpr (NSTR == 2) {
