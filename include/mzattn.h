@@ -141,17 +141,29 @@ typedef struct mzattn_fwd_args {
  * Equivalent to mzattn_fwd_plan followed by mzattn_fwd_execute. */
 int mzattn_fwd(const mzattn_fwd_args* args, void* stream);
 
-/* The two halves of mzattn_fwd, for callers that time or schedule them
- * separately.  mzattn_fwd_plan launches the prepasses, which write the
- * workspace from the mask or segment ids, the positions and K (RoPE table,
- * rotated K, per-tile key ranges / tile classes).  mzattn_fwd_execute
- * launches only the attention kernel and reads that workspace: it must
- * follow a plan with the same arguments, on the same stream (or after it
- * completed), with the workspace, mask, segment ids, positions and K
- * unchanged in between.  Same argument checks and status codes as
- * mzattn_fwd. */
+/* The two halves of mzattn_fwd, for callers that run one layout (mask or
+ * segment ids, positions, RoPE settings, shapes) over many inputs, as a
+ * sampling loop does.
+ *
+ * mzattn_fwd_plan launches the prepasses that depend on the layout only and
+ * writes their results into the workspace: the RoPE cos/sin table (positions
+ * 0 .. max position), per-query key ranges and positions derived from the
+ * segment ids, and the class of every (query tile, key tile) pair of a
+ * boolean mask.  It reads no Q, K or V.
+ *
+ * mzattn_fwd_execute launches the per-input work: the rotation of the K
+ * heads that get RoPE into the workspace, then the attention kernel.  It
+ * must follow a plan with the same arguments on the same stream (or after
+ * the plan completed), with the workspace, mask, segment ids and positions
+ * unchanged since; Q, K, V and O may change between executes.
+ * mzattn_fwd_rotate_k and mzattn_fwd_attend are its two steps, in that
+ * order, for callers that time them separately.
+ *
+ * Same argument checks and status codes as mzattn_fwd. */
 int mzattn_fwd_plan(const mzattn_fwd_args* args, void* stream);
 int mzattn_fwd_execute(const mzattn_fwd_args* args, void* stream);
+int mzattn_fwd_rotate_k(const mzattn_fwd_args* args, void* stream);
+int mzattn_fwd_attend(const mzattn_fwd_args* args, void* stream);
 
 /* Bytes of workspace the call needs (depends on shapes, dtype, mask kind,
  * RoPE); pointer fields are not read.  Returns MZ_OK or a status. */

@@ -120,6 +120,8 @@ _SIGNATURES = {
     "mzattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "mzattn_fwd_plan": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "mzattn_fwd_execute": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "mzattn_fwd_rotate_k": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "mzattn_fwd_attend": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "mzattn_fwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "mzattn_validate_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs)]),
     "mzattn_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
@@ -244,8 +246,9 @@ _WS = _Workspaces()
 
 class FwdCall:
     """A marshalled forward call: the C argument struct plus the tensors it
-    points to (kept alive here).  ``plan()`` / ``execute()`` launch the two
-    halves on the call's stream; ``__call__`` launches both."""
+    points to (kept alive here).  ``plan()`` launches the layout prepasses,
+    ``execute()`` the per-input work (``rotate_k()`` then ``attend()``), all
+    on the call's stream; ``__call__`` launches everything."""
 
     def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
@@ -305,6 +308,16 @@ class FwdCall:
             keep.append(workspace)
         self.args, self.out, self._keep, self._lib = a, o, keep, L
         self.workspace_bytes = need.value
+        self._qkv_shape = [(tuple(x.shape), tuple(x.stride()), x.dtype) for x in (q, k, v)]
+
+    def set_inputs(self, q, k, v):
+        """Point the call at other Q, K, V of the same shapes, strides and
+        dtype (the plan stays valid: it depends on the layout only)."""
+        for x, want in zip((q, k, v), self._qkv_shape):
+            if (tuple(x.shape), tuple(x.stride()), x.dtype) != want:
+                raise MzattnError(MZ_ERR_SHAPE, "replacement input differs in shape, strides or dtype")
+        self.args.q, self.args.k, self.args.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+        self._keep[0], self._keep[1], self._keep[2] = q, k, v
 
     def _launch(self, fn):
         _check(fn(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
@@ -314,6 +327,12 @@ class FwdCall:
 
     def execute(self):
         self._launch(self._lib.mzattn_fwd_execute)
+
+    def rotate_k(self):
+        self._launch(self._lib.mzattn_fwd_rotate_k)
+
+    def attend(self):
+        self._launch(self._lib.mzattn_fwd_attend)
 
     def __call__(self):
         self._launch(self._lib.mzattn_fwd)

@@ -317,7 +317,7 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   p.lse = a->lse;
 }
 
-enum { FWD_PLAN = 1, FWD_MAIN = 2 };
+enum { FWD_PLAN = 1, FWD_ROT = 2, FWD_MAIN = 4 };
 
 int run_fwd(const mzattn_fwd_args* a, void* stream, int parts) {
   FwdPlan pl;
@@ -329,6 +329,7 @@ int run_fwd(const mzattn_fwd_args* a, void* stream, int parts) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (parts & FWD_PLAN) e = mz::launch_fwd_plan(p, s);
+  if (e == hipSuccess && (parts & FWD_ROT)) e = mz::launch_fwd_rotate(p, s);
   if (e == hipSuccess && (parts & FWD_MAIN)) e = mz::launch_fwd_main(p, s);
   if (e != hipSuccess) return fail(MZ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -375,11 +376,15 @@ int mzattn_validate_fwd(const mzattn_fwd_args* args) {
   return st == MZ_OK ? ok() : st;
 }
 
-int mzattn_fwd(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_PLAN | FWD_MAIN); }
+int mzattn_fwd(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_PLAN | FWD_ROT | FWD_MAIN); }
 
 int mzattn_fwd_plan(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_PLAN); }
 
-int mzattn_fwd_execute(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_MAIN); }
+int mzattn_fwd_execute(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_ROT | FWD_MAIN); }
+
+int mzattn_fwd_rotate_k(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_ROT); }
+
+int mzattn_fwd_attend(const mzattn_fwd_args* a, void* stream) { return run_fwd(a, stream, FWD_MAIN); }
 
 int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes) {
   if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");

@@ -976,9 +976,19 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
     const int nkb = (p.Sk + 255) / 256;
     seg_prep_kernel<<<dim3(p.n_qt > nkb ? p.n_qt : nkb, p.B), dim3(256), 0, s>>>(p, bm);
   }
+  if (p.mask_kind == 1) {
+    const int64_t ntiles = (int64_t)p.Bm * p.Hm * p.n_qt * p.n_kt;
+    mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
+  }
+  return hipGetLastError();
+}
+
+// K heads that get RoPE, rotated into the workspace (reads the table and the
+// derived key positions written by the plan).
+hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
   if (p.n_rot_kv > 0) {
     const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-    if (f32) {
+    if (p.dtype == 0) {
       const int rows_per_blk = 256 / (p.D / 2);
       const unsigned nblk = (unsigned)((nrows + rows_per_blk - 1) / rows_per_blk);
       k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
@@ -987,10 +997,6 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
       if (p.dtype == 2) k_rotate16_kernel<BF16><<<dim3(nblk), dim3(256), 0, s>>>(p);
       else k_rotate16_kernel<F16><<<dim3(nblk), dim3(256), 0, s>>>(p);
     }
-  }
-  if (p.mask_kind == 1) {
-    const int64_t ntiles = (int64_t)p.Bm * p.Hm * p.n_qt * p.n_kt;
-    mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
   }
   return hipGetLastError();
 }

@@ -83,6 +83,7 @@ struct DecodeParams {
 };
 
 hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 

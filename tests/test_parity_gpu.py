@@ -280,6 +280,16 @@ def test_plan_then_execute_equals_fwd():
     call.execute()  # executing again over the same plan is allowed
     torch.cuda.synchronize()
     assert torch.equal(call.out, a)
+    # the plan depends on the layout only: new Q/K/V under the same plan
+    # (K rotated again by execute) give what a full call on them gives
+    case2 = W.random_fwd(31, 1, 8, 2, 500, 500, 128, "bf16", W.MASK_SEGMENT, rope_base=1e6, n_segments=3)
+    case2.seg_q, case2.seg_k = case.seg_q, case.seg_k
+    b2 = run_fwd(case2)
+    call.set_inputs(dev(case2.q), dev(case2.k), dev(case2.v))
+    call.rotate_k()
+    call.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(call.out, b2)
 
 
 @pytest.mark.parametrize("S", [4096, 5000])
