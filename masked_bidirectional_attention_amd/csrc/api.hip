@@ -49,6 +49,8 @@ struct FwdPlan {
   int n_rot = 0, n_rot_kv = 0, tab_len = 0;
   int Bm = 1, Hm = 1;
   size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_kpos = 0, off_cls = 0;
+  size_t off_bits = 0;
+  int mask_rows = 0;
   bool need_qpos = false;
   size_t bytes = 0;
 };
@@ -139,7 +141,13 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
       pl->off_kpos = carve((size_t)a->batch * a->seq_k * 4);
     }
   }
-  if (a->mask_kind == MZ_MASK_BOOL) pl->off_cls = carve((size_t)pl->Bm * pl->Hm * pl->n_qt * pl->n_kt);
+  if (a->mask_kind == MZ_MASK_BOOL) {
+    pl->off_cls = carve((size_t)pl->Bm * pl->Hm * pl->n_qt * pl->n_kt);
+    if (a->dtype != MZ_F32) {
+      pl->mask_rows = a->mask_stride[2] == 0 ? 1 : a->seq_q;
+      pl->off_bits = carve((size_t)pl->Bm * pl->Hm * pl->mask_rows * pl->n_kt * 8);
+    }
+  }
   pl->bytes = off == 0 ? 0 : align256(off);
   return MZ_OK;
 }
@@ -303,6 +311,10 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
     p.mask = a->mask;
     for (int i = 0; i < 4; ++i) p.ms[i] = a->mask_stride[i];
     p.tile_cls = reinterpret_cast<uint8_t*>(ws + pl.off_cls);
+    if (a->dtype != MZ_F32) {
+      p.mask_bits = reinterpret_cast<uint64_t*>(ws + pl.off_bits);
+      p.mask_rows = pl.mask_rows;
+    }
     p.mask_vec16 = aligned(a->mask, 16) && a->mask_stride[0] % 16 == 0 && a->mask_stride[1] % 16 == 0 &&
                    a->mask_stride[2] % 16 == 0;
   }

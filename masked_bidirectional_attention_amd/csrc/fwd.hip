@@ -221,30 +221,36 @@ __global__ void mask_tiles_kernel(const FwdParams p, int bm) {
   const int q_lo = qt * bm, k_lo = kt * FWD_BN;
   const int nq = p.ms[2] == 0 ? 1 : min(bm, p.Sq - q_lo);
   const int nk = min(FWD_BN, p.Sk - k_lo);
+  // key bits: written once per mask row (a broadcast row by query tile 0)
+  uint16_t* bits = nullptr;
+  if (p.mask_bits != nullptr && (p.ms[2] != 0 || qt == 0))
+    bits = reinterpret_cast<uint16_t*>(p.mask_bits + ((int64_t)bh * p.mask_rows + (p.ms[2] == 0 ? 0 : q_lo)) * p.n_kt + kt);
   int any = 0, all = 1;
-  if (p.mask_vec16 && nk == FWD_BN) {
-    // rows are 16-byte aligned: 4 x 16 bytes per row
-    for (int idx = threadIdx.x; idx < nq * 4; idx += blockDim.x) {
-      const int r = idx >> 2, c = idx & 3;
-      const uint4 v = *(const uint4*)(base + (int64_t)(q_lo + r) * p.ms[2] + k_lo + c * 16);
+  // one item = 16 keys of one row: 16 key bits, and their share of the class
+  for (int idx = threadIdx.x; idx < nq * 4; idx += blockDim.x) {
+    const int r = idx >> 2, c = idx & 3;
+    const uint8_t* row = base + (int64_t)(q_lo + r) * p.ms[2] + k_lo + c * 16;
+    const int n = min(16, nk - c * 16);  // keys of this item below Sk
+    uint32_t m16 = 0;
+    if (p.mask_vec16 && n == 16) {
+      const uint4 v = *(const uint4*)row;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // a byte is live iff nonzero
+        // high bit of each byte = byte != 0
         const uint32_t x = w[e];
-        const uint32_t nz = ((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x;  // high bit of each byte = byte != 0
-        const uint32_t hi = nz & 0x80808080u;
-        any |= hi != 0;
-        all &= hi == 0x80808080u;
+        const uint32_t hi = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+        m16 |= (((hi >> 7) & 1u) | ((hi >> 14) & 2u) | ((hi >> 21) & 4u) | ((hi >> 28) & 8u)) << (4 * e);
       }
+    } else {
+      for (int e = 0; e < n; ++e) m16 |= (uint32_t)(row[e] != 0) << e;
     }
-  } else {
-    for (int idx = threadIdx.x; idx < nq * nk; idx += blockDim.x) {
-      const int r = idx / nk, c = idx % nk;
-      const int v = base[(int64_t)(q_lo + r) * p.ms[2] + k_lo + c] != 0;
-      any |= v;
-      all &= v;
+    if (n > 0) {
+      const uint32_t full = n == 16 ? 0xFFFFu : ((1u << n) - 1u);
+      any |= m16 != 0;
+      all &= m16 == full;
     }
+    if (bits != nullptr) bits[(int64_t)r * p.n_kt * 4 + c] = (uint16_t)m16;
   }
   any = __syncthreads_or(any);
   all = __syncthreads_and(all);
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   int kt_beg = 0, kt_end = p.n_kt, full_beg = 0, full_end = 0;
   int lo = 0, hi = p.Sk;
   const uint8_t* cls_row = nullptr;
-  const uint8_t* mrow = nullptr;
+  const uint64_t* brow = nullptr;  // this lane's key-bit words (valid queries)
   bool cls_in_lds = false;
   if constexpr (MK == 2) {
     const int4 r = p.qt_range[(int64_t)b * p.n_qt + qt];
@@ -391,7 +397,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   } else if constexpr (MK == 1) {
     const int bm_ = p.Bm == 1 ? 0 : b, hm_ = p.Hm == 1 ? 0 : h;
     cls_row = p.tile_cls + ((int64_t)(bm_ * p.Hm + hm_) * p.n_qt + qt) * p.n_kt;
-    if (qvalid) mrow = p.mask + b * p.ms[0] + h * p.ms[1] + (int64_t)qi * p.ms[2];
+    if (qvalid)
+      brow = p.mask_bits + ((int64_t)(bm_ * p.Hm + hm_) * p.mask_rows + (p.ms[2] == 0 ? 0 : qi)) * p.n_kt;
     cls_in_lds = p.n_kt <= CLS_LDS;
     if (cls_in_lds) {
       for (int i = tid; i < p.n_kt; i += NT) cls_lds[i] = cls_row[i];
@@ -532,7 +539,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       const int base = kt * BN + hh * 4;
       const int lim = p.Sk - base;       // keys past Sk
       const int lo_t = lo - base, hi_t = hi - base;
-      const uint8_t* mb = mrow != nullptr ? mrow + base : nullptr;
+      // the lane's key bits of this tile, shifted to its half (keys past Sk
+      // carry 0 bits); lanes without a query see none live
+      uint64_t kbits = 0;
+      if constexpr (MK == 1) {
+        if (brow != nullptr) kbits = brow[kt] >> (hh * 4);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           const int c = kb * 32 + (v >> 2) * 8 + (v & 3);
           bool live;
           if constexpr (MK == 2) live = c >= lo_t && c < hi_t;
-          else if constexpr (MK == 1) live = c < lim && mb != nullptr && mb[c] != 0;
+          else if constexpr (MK == 1) live = (kbits >> c) & 1;
           else live = c < lim;
           sc[kb][v] = live ? sc[kb][v] : -INFINITY;
         }

@@ -45,6 +45,10 @@ struct FwdParams {
   int Bm, Hm;
   int mask_vec16;
   uint8_t* tile_cls;  // [Bm][Hm][n_qt][n_kt]
+  // [Bm][Hm][mask_rows][n_kt] key bits of every (query, key tile): bit c of
+  // word (i, t) is key t * FWD_BN + c (0 past Sk).  16-bit kernels only.
+  uint64_t* mask_bits;
+  int mask_rows;  // Sq, or 1 for a mask broadcast over queries
   // segments
   const int32_t* seg_q;
   const int32_t* seg_k;
