@@ -87,9 +87,9 @@ __device__ inline void fold_into(Part2& x, float m, float l, float a0, float a1)
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one work-group per (batch, kv-head, row).  Chunks are taken
-// in super-groups of 64; within one, thread group g holds chunks
-// [g*CG, (g+1)*CG) of it.  The super-group's maximum m over its live chunks
+// Merge kernel: one work-group per (batch, kv-head, row, slice of DS d
+// pairs).  Chunks are taken in super-groups of 64; within one, thread group
+// g holds chunks [g*CG, (g+1)*CG) of it.  The super-group's maximum m over its live chunks
 // (l > 0) is exact; every live chunk then contributes its l and acc scaled
 // by 2^(m_c - m), summed in chunk order within a group and in group order
 // across groups; super-groups are folded in order.  Chunks at or past
@@ -97,17 +97,20 @@ __device__ inline void fold_into(Part2& x, float m, float l, float a0, float a1)
 // the identity of the fold, so the result does not depend on how many
 // chunks the span covered beyond its live keys.
 // ---------------------------------------------------------------------------
+constexpr int MERGE_DS = 16;  // d pairs per merge work-group
+
 template <int D, typename Store>
 __device__ void decode_merge_row(const DecodeParams& p, Store store) {
-  constexpr int HD = D / 2;     // d pairs
-  constexpr int NG = 256 / HD;  // chunk groups (4 for D 128, 8 for D 64)
-  constexpr int CG = 64 / NG;   // chunks per group per super-group
+  constexpr int HD = MERGE_DS;  // d pairs of this work-group
+  constexpr int NS = D / 2 / HD;  // slices per row
+  constexpr int NG = 256 / HD;  // chunk groups (16)
+  constexpr int CG = 64 / NG;   // chunks per group per super-group (4)
   __shared__ float gmax[NG];
   __shared__ Part2 red[256];
-  const int row = blockIdx.x;  // (unit, n)
+  const int row = blockIdx.x / NS, slice = blockIdx.x % NS;  // (unit, n), d slice
   const int n = row % p.R, unit = row / p.R;
   const int kvh = unit % p.Hkv, b = unit / p.Hkv;
-  const int t = threadIdx.x, dp = t % HD, g = t / HD;
+  const int t = threadIdx.x, dp = slice * HD + t % HD, g = t / HD;
   const float2* ml = p.part_ml + (int64_t)unit * p.n_chunks * p.R + n;
   const float* pa = p.part_acc + ((int64_t)unit * p.n_chunks * p.R + n) * D + 2 * dp;
   Part2 tot = {0.f, 0.f, 0.f, 0.f};
@@ -129,7 +132,7 @@ __device__ void decode_merge_row(const DecodeParams& p, Store store) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CG; ++i) mx = mc[i].y > 0.f ? fmaxf(mx, mc[i].x) : mx;
-    if (dp == 0) gmax[g] = mx;
+    if (t % HD == 0) gmax[g] = mx;
     __syncthreads();
     float m = gmax[0];
 #pragma unroll
@@ -145,10 +148,10 @@ __device__ void decode_merge_row(const DecodeParams& p, Store store) {
     red[t] = x;
     __syncthreads();
     if (g == 0) {
-      Part2 y = red[dp];
+      Part2 y = red[t];
 #pragma unroll
       for (int gg = 1; gg < NG; ++gg) {
-        const Part2 z = red[gg * HD + dp];
+        const Part2 z = red[gg * HD + t];
         y.l += z.l;
         y.a0 += z.a0;
         y.a1 += z.a1;
@@ -476,7 +479,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
     else decode_q_rotate16_kernel<F16><<<dim3(nb), dim3(256), 0, s>>>(p);
   }
   const unsigned nblk = (unsigned)((int64_t)p.B * p.Hkv * p.n_chunks);
-  const unsigned nrows = (unsigned)((int64_t)p.B * p.Hkv * p.R);
+  const unsigned nrows = (unsigned)((int64_t)p.B * p.Hkv * p.R * (p.D / 2 / MERGE_DS));
   if (p.dtype == 0) {
     decode_f32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
     if (p.D == 64) decode_merge32_kernel<64><<<dim3(nrows), dim3(256), 0, s>>>(p);
