@@ -612,14 +612,11 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     pv_all(vstage);
   };
 
-  // Steady-state step, merged: the 2*NS MFMAs of K Q^T for t(j+1) (two
-  // accumulator chains) alternate with the 4*ND MFMAs of P.V for t(j) (ND
-  // chains), so consecutive MFMAs of one chain sit several slots apart and
-  // no MFMA waits on the latency of its predecessor.  P block (kb, jj) is
-  // produced by exponential pieces in the slots before the first P.V MFMA
-  // that reads it; the copies of the step take odd slots.
+  // One exponential piece: 2 of the 32 scores of a lane (tile t(j)), packed
+  // into P block (kb, jj) and added to the row sum.
   constexpr int NQK = 2 * NS, NPV = 4 * ND;
-  static_assert(NQK == NPV, "alternating schedule");
+  static_assert(16 % NQK == 0, "exponential pieces spread evenly over the K Q^T MFMAs");
+  static_assert(NSLOT <= NPV, "every copy has a P.V slot");
   auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4], f32x16_t (&scur)[2]) {
     constexpr int h = decltype(hc)::value;
     constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
@@ -631,13 +628,20 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
     if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
   };
-  auto step_merged = [&](int kstage, int vstage, const DmaPlan& pl, f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
+
+  float mx = -INFINITY;  // row max of the newest scores
+  // Steady-state step, split: the 2*NS K Q^T MFMAs of t(j+1) come first,
+  // one exponential piece of t(j) after each (P block (kb, jj) is complete
+  // before the P.V half starts); then the 4*ND P.V MFMAs of t(j) with the
+  // copies of the step and, once the K Q^T results have landed, the mask and
+  // row max of t(j+1) (after the half for boolean masks), so that the next
+  // step does not wait on them.
+  auto step_split = [&](int kstage, int vstage, const DmaPlan& pl, f32x16_t (&scur)[2], f32x16_t (&snext)[2],
+                        int kt_next) {
     const uint16_t* kt_lds = &Ks[str][kstage][0];
     const uint16_t* vt_lds = &Vs[str][vstage][0];
     float lsa = 0.f, lsb = 0.f;
     uint32_t wv[2][2][4];
-    // P block (0, 0) before the first P.V MFMA
-    static_for<4>([&](auto hc) { exp_piece(hc, lsa, lsb, wv, scur); });
     auto kfrag = [&](auto gc) -> uint4 {
       constexpr int g = decltype(gc)::value, ss = g >> 1, kb = g & 1;
       return *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * ss + hh) * 8];
@@ -651,33 +655,34 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       return make_uint4(a0.x, a0.y, a1.x, a1.y);
     };
     uint4 frk[PF], frv[PF];
-    static_for<PF>([&](auto gc) {
-      frk[decltype(gc)::value] = kfrag(gc);
-      frv[decltype(gc)::value] = vfrag(gc);
+    static_for<PF>([&](auto gc) { frk[decltype(gc)::value] = kfrag(gc); });
+    static_for<NQK>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, ss = i >> 1, kb = i & 1;
+      const uint4 f = frk[i % PF];
+      if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
+      else frv[i + PF - NQK] = vfrag(std::integral_constant<int, i + PF - NQK>{});
+      snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? (CINIT ? cinit : zero16) : snext[kb]);
+      static_for<16 / NQK>([&](auto pc) { exp_piece(std::integral_constant<int, i * (16 / NQK) + decltype(pc)::value>{}, lsa, lsb, wv, scur); });
+      __builtin_amdgcn_sched_barrier(0);
     });
-    // slot 2i: K Q^T MFMA i; slot 2i+1: P.V MFMA i
-    static_for<2 * NQK>([&](auto uc) {
-      constexpr int u = decltype(uc)::value, i = u >> 1;
-      if constexpr ((u & 1) == 0) {
-        constexpr int ss = i >> 1, kb = i & 1;
-        const uint4 f = frk[i % PF];
-        if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
-        snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? (CINIT ? cinit : zero16) : snext[kb]);
-        // exponential pieces of P blocks (0,1), (1,0), (1,1): piece h in
-        // slot 2 * (h - 4) * NQK / 12 + 2, before the P.V MFMAs reading it
-        static_for<16>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          if constexpr (h >= 4 && 2 * ((h - 4) * (NQK - 2) / 12) == u) exp_piece(hc, lsa, lsb, wv, scur);
-        });
-      } else {
-        constexpr int kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
-        const uint4 f = frv[i % PF];
-        if constexpr (i + PF < NPV) frv[i % PF] = vfrag(std::integral_constant<int, i + PF>{});
-        oacc[db] = mfma32<T>(f, pk[kb][jj], oacc[db]);
-        if constexpr (i >= 1 && i - 1 < NSLOT) dma_slot(pl, i - 1);
+    static_for<NPV>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
+      const uint4 f = frv[i % PF];
+      if constexpr (i + PF < NPV) frv[i % PF] = vfrag(std::integral_constant<int, i + PF>{});
+      oacc[db] = mfma32<T>(f, pk[kb][jj], oacc[db]);
+      if constexpr (i < NSLOT) dma_slot(pl, i);
+      if constexpr (i == 3 && MK != 1) {
+        mask_tile(kt_next, snext);
+        mx = rowmax(snext);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // boolean masks: a mixed tile loads its key bits, a wait that would
+    // also cover the copies just issued, so it comes after the P.V half
+    if constexpr (MK == 1) {
+      mask_tile(kt_next, snext);
+      mx = rowmax(snext);
+    }
     l_run += lsa + lsb;
   };
 
@@ -699,7 +704,6 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   if (kn < kt_end) load_k(kn, 1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  float mx = -INFINITY;
   auto rescale_step = [&](f32x16_t (&sc)[2]) {
     // ---- online softmax with lazy rescaling.  The reference m of a query
     // moves only when a score exceeds it by more than 2^8 (otherwise the
@@ -756,9 +760,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
     const DmaPlan pl = plan_step(kn2);
     rescale_step(sc);
-    step_merged((j + 1) & 1, j & 1, pl, sc, sn);
-    mask_tile(kn, sn);
-    mx = rowmax(sn);
+    step_split((j + 1) & 1, j & 1, pl, sc, sn, kn);
     kt = kn;
     kn = kn2;
     ++j;
