@@ -25,7 +25,8 @@ forward of three speech engines:
 * VoxCPM page, "What matches upstream" (attention): each generation step
   attends to a static KV cache under an explicit boolean mask; masked
   positions add exact zeros, so cutting the key span anywhere past the
-  last live key leaves the result unchanged.
+  last live key leaves the result unchanged.  The same bullet runs the
+  prefill through SDPA with a causal mask (the ``causal`` kind here).
 
 The oracle is the plain definition, written out in fp64 (tiling and an
 online softmax are exact reformulations of it, so there is no algorithm
@@ -40,7 +41,9 @@ to follow step by step):
 Readings where the pages are silent (each is listed in the design doc):
 True in a mask means "takes part"; a query with no live key gives 0;
 interleaved RoPE rotates adjacent pairs (2i, 2i+1) by pos * base^(-2i/D);
-with GQA, query head h reads K/V head floor(h / G).
+with GQA, query head h reads K/V head floor(h / G); causal follows SDPA's
+is_causal, key j live for query i iff j <= i (aligned at the top-left
+corner also when Sq != Sk).
 
 Inputs are raw storage bits (uint16 for fp16/bf16, uint32 for fp32); the
 oracle decodes them exactly to fp64 and never rounds afterwards.
@@ -179,13 +182,18 @@ def live_set_fwd(B, Hq, Sq, Sk, mask_kind, mask=None, seg_q=None, seg_k=None):
     OmniVoice page, attention-mask bullet), broadcast over size-1 dims.
     'segment': query i and key j of one row are live together iff both
     carry the same non-negative id (the block-diagonal mask of the
-    OmniVoice page's packed_guidance mode)."""
+    OmniVoice page's packed_guidance mode).  'causal': key j is live for
+    query i iff j <= i (the prefill of the VoxCPM page's attention bullet,
+    SDPA's is_causal convention)."""
     if mask_kind == "none":
         return np.ones((B, 1, Sq, Sk), dtype=bool)
     if mask_kind == "bool":
         m = np.asarray(mask, dtype=bool)
         assert m.ndim == 4 and m.shape[3] == Sk
         return np.broadcast_to(m, (B, m.shape[1], Sq, Sk))
+    if mask_kind == "causal":
+        live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]
+        return np.broadcast_to(live, (B, 1, Sq, Sk))
     if mask_kind == "segment":
         sq = np.broadcast_to(np.asarray(seg_q), (B, Sq))
         sk = np.broadcast_to(np.asarray(seg_k), (B, Sk))

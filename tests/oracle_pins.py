@@ -172,6 +172,35 @@ def pin_sdpa_bool_masks():
         _close(o, ref, 1e-12, f"sdpa {mshape}")
 
 
+def _sdpa_causal(q, k, v, scale=None, gqa=False):
+    """torch CPU SDPA in fp64 with is_causal (library routine)."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
+    return F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale, enable_gqa=gqa).numpy()
+
+
+def pin_sdpa_causal():
+    """Causal kind against torch's CPU SDPA is_causal in fp64, for square
+    and non-square shapes (SDPA aligns the causal band at the top-left
+    corner), with GQA and an explicit scale."""
+    rng = np.random.default_rng(21)
+    for (B, Hq, Hkv, Sq, Sk, D, scale) in ((2, 4, 4, 13, 13, 8, 0.0), (1, 6, 2, 9, 21, 16, 0.3),
+                                           (2, 4, 1, 20, 7, 32, 0.0), (1, 2, 2, 1, 5, 8, 0.0)):
+        q, k, v = _rand(rng, B, Hq, Sq, D), _rand(rng, B, Hkv, Sk, D), _rand(rng, B, Hkv, Sk, D)
+        o, _ = mzref.mzref_fwd("f32", _bits64(q), _bits64(k), _bits64(v), scale=scale, mask_kind="causal")
+        ref = _sdpa_causal(q, k, v, scale if scale > 0 else None, gqa=Hq != Hkv)
+        _close(o, ref, 1e-12, f"sdpa causal {Sq}x{Sk}")
+
+
+def pin_causal_first_query_is_v0():
+    """Closed form: query 0 sees key 0 alone, so its output is v_0 exactly
+    and its log-sum-exp is its one score."""
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 1, 2, 6, 8), _rand(rng, 1, 2, 9, 8), _rand(rng, 1, 2, 9, 8)
+    o, lse = mzref.mzref_fwd("f32", _bits64(q), _bits64(k), _bits64(v), mask_kind="causal")
+    assert np.array_equal(o[0, :, 0], v[0, :, 0])
+    _close(lse[0, :, 0], np.einsum("hd,hd->h", q[0, :, 0], k[0, :, 0]) / math.sqrt(8), 1e-12, "causal lse q0")
+
+
 def pin_sdpa_no_mask():
     rng = np.random.default_rng(5)
     q, k, v = _rand(rng, 2, 4, 11, 32), _rand(rng, 2, 4, 19, 32), _rand(rng, 2, 4, 19, 32)
@@ -397,4 +426,5 @@ ALL_PINS = [
     pin_key_permutation, pin_masked_garbage, pin_gqa_is_repeat, pin_partial_rope_heads,
     pin_packed_equals_separate, pin_segment_positions, pin_segment_padding,
     pin_decode_vs_sdpa_truncated, pin_decode_span_invariance, pin_decode_rope_q,
+    pin_sdpa_causal, pin_causal_first_query_is_v0,
 ]

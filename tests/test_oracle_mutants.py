@@ -41,6 +41,12 @@ MUTANTS = {
     "fp16_bias": ("(e - 15)", "(e - 14)"),
     "fp16_subnormal": ("sub = np.ldexp(f, -24)", "sub = np.ldexp(f, -23)"),
     "empty_row_nan": ("o = np.zeros((q.shape[0], v.shape[1]))", "o = np.full((q.shape[0], v.shape[1]), np.nan)"),
+    "causal_strict": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
+                      "live = np.arange(Sk)[None, :] < np.arange(Sq)[:, None]"),
+    "causal_bottom_right": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
+                            "live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq)"),
+    "causal_transposed": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
+                          "live = np.arange(Sk)[None, :] >= np.arange(Sq)[:, None]"),
 }
 
 
