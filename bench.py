@@ -291,6 +291,29 @@ def main(argv=None):
             by_fill.append({"fill": L, "span": span, "us": round(us, 2),
                             "GB/s": round(decode_bytes(L, span) / (us * 1e-6) / 1e9, 1),
                             "algorithmic_mb": round(decode_bytes(L, span) / 1e6, 3)})
+    # ---- causal prefill (reported, not the headline): the same kernel under
+    # the causal kind, K rotation + attention per call, layout planned once
+    cp = W.vox_prefill_causal()
+    cpf = mz.FwdCall(cp.q.to(dev), cp.k.to(dev), cp.v.to(dev), causal=True, rope_base=cp.rope_base,
+                     scale=cp.scale)
+    cpf.plan()
+    for _ in range(5):
+        cpf.execute()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(50):
+        cpf.execute()
+    e1.record()
+    torch.cuda.synchronize()
+    cp_us = e0.elapsed_time(e1) / 50 * 1e3
+    B_, Hq_, S_ = cp.q.shape[0], cp.q.shape[1], cp.q.shape[2]
+    cp_gflop = 4 * 128 * B_ * Hq_ * S_ * (S_ + 1) / 2 / 1e9
+    causal = {"workload": f"causal prefill: B {B_}, {S_} tokens, Hq 16 / Hkv 2, D 128, bf16, RoPE base 1e4",
+              "execute_us": round(cp_us, 2), "live_gflop": round(cp_gflop, 3),
+              "TFLOP/s": round(cp_gflop / cp_us * 1e3, 1),
+              "frac": round(cp_gflop / cp_us * 1e3 / PEAK_BF16_TFLOPS, 4)}
+
     traffic = {}
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
@@ -352,6 +375,7 @@ def main(argv=None):
             },
             "by_fill": by_fill,
         },
+        "causal_prefill": causal,
         "device": props.name,
     }
     if not a.no_cpu_baseline:

@@ -79,7 +79,10 @@ typedef enum mz_dtype { MZ_F32 = 0, MZ_F16 = 1, MZ_BF16 = 2 } mz_dtype;
 typedef enum mz_mask_kind {
   MZ_MASK_NONE = 0,    /* every key is live                                  */
   MZ_MASK_BOOL = 1,    /* live(b,h,i,j) = mask[b,h,i,j] != 0                 */
-  MZ_MASK_SEGMENT = 2  /* live(b,i,j) = seg_q[b,i] >= 0 && seg_q[b,i] == seg_k[b,j] */
+  MZ_MASK_SEGMENT = 2, /* live(b,i,j) = seg_q[b,i] >= 0 && seg_q[b,i] == seg_k[b,j] */
+  MZ_MASK_CAUSAL = 3   /* live(i,j) = j <= i (top-left aligned, as SDPA's is_causal;
+                          the prefill of the VoxCPM page, "What matches upstream",
+                          attention bullet); mask and seg pointers are ignored */
 } mz_mask_kind;
 
 /* ---- mzattn_fwd -------------------------------------------------------- */

@@ -30,7 +30,7 @@ MZ_ERR_HIP = -9
 MZ_ERR_VALUE = -10
 
 MZ_F32, MZ_F16, MZ_BF16 = 0, 1, 2
-MZ_MASK_NONE, MZ_MASK_BOOL, MZ_MASK_SEGMENT = 0, 1, 2
+MZ_MASK_NONE, MZ_MASK_BOOL, MZ_MASK_SEGMENT, MZ_MASK_CAUSAL = 0, 1, 2, 3
 
 _i64x3 = ctypes.c_int64 * 3
 _i64x4 = ctypes.c_int64 * 4
@@ -250,7 +250,7 @@ class FwdCall:
     ``execute()`` the per-input work (``rotate_k()`` then ``attend()``), all
     on the call's stream; ``__call__`` launches everything."""
 
-    def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
+    def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                  out=None, return_lse: bool = False, workspace=None, stream=None):
         torch = _torch()
@@ -270,9 +270,11 @@ class FwdCall:
         a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
         a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
         keep = [q, k, v, o]
-        if mask is not None and seg_q is not None:
-            raise MzattnError(MZ_ERR_UNSUPPORTED, "give either mask or segment ids")
-        if mask is not None:
+        if (mask is not None) + (seg_q is not None) + bool(causal) > 1:
+            raise MzattnError(MZ_ERR_UNSUPPORTED, "give at most one of mask, segment ids, causal")
+        if causal:
+            a.mask_kind = MZ_MASK_CAUSAL
+        elif mask is not None:
             a.mask_kind = MZ_MASK_BOOL
             m, st = _mask_strides(mask, B, Hq, Sq, Sk)
             a.mask, a.mask_stride = m.data_ptr(), st
@@ -339,14 +341,15 @@ class FwdCall:
         return (self.out, self.lse) if self.lse is not None else self.out
 
 
-def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, pos_q=None, pos_k=None,
+def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                out=None, return_lse: bool = False, workspace=None, stream=None):
     """Masked bidirectional attention forward (see ``mzattn_fwd`` in
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
     same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
-    [B, S] (segment mode).  Returns o (and lse when ``return_lse``)."""
-    return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, pos_q=pos_q, pos_k=pos_k,
+    [B, S] (segment mode); causal: key j live for query i iff j <= i.
+    Returns o (and lse when ``return_lse``)."""
+    return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, causal=causal, pos_q=pos_q, pos_k=pos_k,
                    scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, out=out,
                    return_lse=return_lse, workspace=workspace, stream=stream)()
 

@@ -83,7 +83,8 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
     return fail(MZ_ERR_SHAPE, "seq_q %d / seq_k %d outside [0, %lld]", a->seq_q, a->seq_k, (long long)kMaxSeq);
   if (a->head_dim != 64 && a->head_dim != 128)
     return fail(MZ_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", a->head_dim);
-  if (a->mask_kind != MZ_MASK_NONE && a->mask_kind != MZ_MASK_BOOL && a->mask_kind != MZ_MASK_SEGMENT)
+  if (a->mask_kind != MZ_MASK_NONE && a->mask_kind != MZ_MASK_BOOL && a->mask_kind != MZ_MASK_SEGMENT &&
+      a->mask_kind != MZ_MASK_CAUSAL)
     return fail(MZ_ERR_UNSUPPORTED, "unknown mask_kind %d", a->mask_kind);
   if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
   if (!isfinite(a->rope_base) || a->rope_base < 0.0)

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   const int nwork = p.B * p.Hq * p.n_qt;
   const int w = xcd_remap(blockIdx.x, nwork);
   const int g = w % p.G;
-  const int qt = (w / p.G) % p.n_qt;
+  // causal: the last query tiles have the most keys, so they start first
+  const int qt = MK == 3 ? p.n_qt - 1 - (w / p.G) % p.n_qt : (w / p.G) % p.n_qt;
   const int kvb = w / (p.G * p.n_qt);
   const int b = kvb % p.B, hk = kvb / p.B;
   const int h = hk * p.G + g;
@@ -394,6 +395,14 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     } else {
       lo = 0; hi = 0;
     }
+  } else if constexpr (MK == 3) {
+    // causal: keys [0, i] of query i; whole tiles below the tile's first
+    // query need no per-element test
+    const int q_first = qt * BM, q_last = min(p.Sq, q_first + BM) - 1;
+    kt_end = (min(p.Sk, q_last + 1) + BN - 1) / BN;
+    full_end = min(p.Sk, q_first + 1) / BN;
+    lo = 0;
+    hi = qvalid ? min(p.Sk, qi + 1) : 0;
   } else if constexpr (MK == 1) {
     const int bm_ = p.Bm == 1 ? 0 : b, hm_ = p.Hm == 1 ? 0 : h;
     cls_row = p.tile_cls + ((int64_t)(bm_ * p.Hm + hm_) * p.n_qt + qt) * p.n_kt;
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // per-tile thresholds, so no per-register key offset stays in registers.
   auto mask_tile = [&](int kt, f32x16_t (&sc)[2]) {
     bool check;
-    if constexpr (MK == 2) check = !(kt >= full_beg && kt < full_end);
+    if constexpr (MK == 2 || MK == 3) check = !(kt >= full_beg && kt < full_end);
     else if constexpr (MK == 1) check = cls_at(kt) == 2 || kt >= first_tail_tile;
     else check = kt >= first_tail_tile;
     if (__builtin_expect(check, 0)) {
@@ -551,7 +560,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         for (int v = 0; v < 16; ++v) {
           const int c = kb * 32 + (v >> 2) * 8 + (v & 3);
           bool live;
-          if constexpr (MK == 2) live = c >= lo_t && c < hi_t;
+          if constexpr (MK == 2 || MK == 3) live = c >= lo_t && c < hi_t;
           else if constexpr (MK == 1) live = (kbits >> c) & 1;
           else live = c < lim;
           sc[kb][v] = live ? sc[kb][v] : -INFINITY;
@@ -917,6 +926,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
     const int bm_ = p.Bm == 1 ? 0 : b, hm_ = p.Hm == 1 ? 0 : h;
     cls_row = p.tile_cls + ((int64_t)(bm_ * p.Hm + hm_) * p.n_qt + qt) * p.n_kt;
     if (qvalid) mrow = p.mask + b * p.ms[0] + h * p.ms[1] + (int64_t)qi * p.ms[2];
+  } else if (p.mask_kind == 3) {
+    // causal: keys [0, i]; tiles past the tile's last query are skipped
+    const int q_last = min(p.Sq, qt * BM + BM) - 1;
+    kt_end = (min(p.Sk, q_last + 1) + FWD_BN - 1) / FWD_BN;
+    lo = 0;
+    hi = qvalid ? min(p.Sk, qi + 1) : 0;
   }
 
   float o[D];
@@ -942,7 +957,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
       for (int r = 0; r < SUB; ++r) {
         const int key = key0 + r;
         bool live;
-        if (p.mask_kind == 2) live = key >= lo && key < hi;
+        if (p.mask_kind == 2 || p.mask_kind == 3) live = key >= lo && key < hi;
         else if (p.mask_kind == 1) live = key < p.Sk && mrow != nullptr && mrow[key] != 0;
         else live = key < p.Sk;
         float acc = 0.f;
@@ -1018,7 +1033,8 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
 template <typename T, int D, int NSTR>
 static void launch_mfma_n(const FwdParams& p, unsigned nwork, hipStream_t s) {
   const dim3 blk(256 * NSTR);
-  if (p.mask_kind == 2) fwd_mfma_kernel<T, D, 2, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
+  if (p.mask_kind == 3) fwd_mfma_kernel<T, D, 3, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
+  else if (p.mask_kind == 2) fwd_mfma_kernel<T, D, 2, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
   else if (p.mask_kind == 1) fwd_mfma_kernel<T, D, 1, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
   else fwd_mfma_kernel<T, D, 0, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
 }

@@ -39,7 +39,7 @@ import torch
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 DTYPE_NAME = {v: k for k, v in DTYPES.items()}
 
-MASK_NONE, MASK_BOOL, MASK_SEGMENT = "none", "bool", "segment"
+MASK_NONE, MASK_BOOL, MASK_SEGMENT, MASK_CAUSAL = "none", "bool", "segment", "causal"
 
 
 @dataclasses.dataclass
@@ -193,6 +193,23 @@ def ceil256(n: int) -> int:
     """Span rounding for the static cache: the first multiple of 256 at or
     after the current length (VoxCPM page, 'What matches upstream')."""
     return -(-n // 256) * 256
+
+
+VOX_PREFILL = 2048
+
+
+def vox_prefill_causal(seed: int = 5) -> FwdCase:
+    """bf16 causal prefill in the VoxCPM text-semantic LM's head layout
+    (the decode step's: Hq 16 / Hkv 2, D 128): B 2 (guidance pair), 2048
+    tokens, N(0,1) q/k/v, interleaved RoPE base 1e4 (the LM's LongRoPE
+    factors are not modelled)."""
+    B, Hq, Hkv, S, D = 2, 16, 2, VOX_PREFILL, 128
+    gen = torch.Generator().manual_seed(seed)
+    q = _randn(gen, (B, Hq, S, D), "bf16")
+    k = _randn(gen, (B, Hkv, S, D), "bf16")
+    v = _randn(gen, (B, Hkv, S, D), "bf16")
+    return FwdCase("vox_prefill_causal_bf16", "bf16", q, k, v, scale=1.0 / math.sqrt(D),
+                   rope_base=1e4, pe_attn_head=-1, mask_kind=MASK_CAUSAL)
 
 
 def vox_decode(filled: int, span: Optional[int] = None, seed: int = 4) -> DecodeCase:

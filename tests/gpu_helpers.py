@@ -26,6 +26,8 @@ def run_fwd(case: W.FwdCase, return_lse=False, q=None, k=None, v=None):
         kw["mask"] = dev(case.mask)
     elif case.mask_kind == W.MASK_SEGMENT:
         kw["seg_q"], kw["seg_k"] = dev(case.seg_q), dev(case.seg_k)
+    elif case.mask_kind == W.MASK_CAUSAL:
+        kw["causal"] = True
     out = mz.mzattn_fwd(q, k, v, **kw)
     torch.cuda.synchronize()
     return out

@@ -124,6 +124,11 @@ def test_fwd_valid_variants(lib):
     a.mask_stride = B._i64x4(300, 0, 0, 1)
     with_workspace(L, a)
     assert vfwd(L, a) == 0
+    # causal: no mask or segment pointers needed, no extra workspace
+    a = good_fwd()
+    a.mask_kind = B.MZ_MASK_CAUSAL
+    with_workspace(L, a)
+    assert vfwd(L, a) == 0
     # empty problems are legal no-ops even with NULL tensors
     e = good_fwd(Sq=0)
     e.q = e.o = None
