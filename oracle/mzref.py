@@ -123,6 +123,30 @@ def rope_interleaved(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return out
 
 
+def rope_half_split(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate the pairs (x_i, x_i+D/2) of every row of x [..., S, D] by the
+    angle pos * theta_i: the "rotate half" pairing of GPT-NeoX / Llama-style
+    models, offered beside the interleaved one (the pages' other models; the
+    survey's RoPE-variants item).  Same frequencies and rotation sense."""
+    D = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., :D // 2], x[..., D // 2:]
+    out = np.empty_like(x)
+    out[..., :D // 2] = x0 * c - x1 * s
+    out[..., D // 2:] = x1 * c + x0 * s
+    return out
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float, style: str = "interleaved") -> np.ndarray:
+    """The rotation of one pairing: 'interleaved' (default) or 'half'."""
+    if style == "interleaved":
+        return rope_interleaved(x, pos, base)
+    if style == "half":
+        return rope_half_split(x, pos, base)
+    raise ValueError(style)
+
+
 def segment_positions(seg: np.ndarray) -> np.ndarray:
     """Positions that restart at 0 at the start of every run of equal ids
     (OmniVoice page, 'Memory and speed': each packed block has its own
@@ -205,7 +229,7 @@ def live_set_fwd(B, Hq, Sq, Sk, mask_kind, mask=None, seg_q=None, seg_k=None):
 def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
               rope_base: float = 0.0, pe_attn_head: int = -1,
               pos_q=None, pos_k=None, mask_kind: str = "none", mask=None,
-              seg_q=None, seg_k=None, heads=None):
+              seg_q=None, seg_k=None, heads=None, rope_style: str = "interleaved"):
     """Oracle of the bidirectional forward.
 
     q_bits [B, Hq, Sq, D], k_bits / v_bits [B, Hkv, Sk, D] (storage bits
@@ -216,6 +240,7 @@ def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
     K/V heads they read; positions default to 0..S-1, or in segment mode
     to the index within the segment.  ``heads``: optional list of query
     heads to evaluate (others are left 0), for sampling large shapes.
+    ``rope_style``: 'interleaved' (adjacent pairs) or 'half' (x_i, x_i+D/2).
 
     Returns (o [B, Hq, Sq, D], lse [B, Hq, Sq]) in fp64.
     """
@@ -253,15 +278,15 @@ def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
             hk = h // G
             qh, kh, vh = q[b, h], k[b, hk], v[b, hk]
             if h < n_rot:
-                qh = rope_interleaved(qh, pq[b], rope_base)
-                kh = rope_interleaved(kh, pk[b], rope_base)
+                qh = rope(qh, pq[b], rope_base, rope_style)
+                kh = rope(kh, pk[b], rope_base, rope_style)
             lv = live[b, h if live.shape[1] > 1 else 0]
             o[b, h], lse[b, h] = attend(qh, kh, vh, lv, scale)
     return o, lse
 
 
 def mzref_decode(dtype: str, q_bits, k_bits, v_bits, *, span: int, mask=None,
-                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None):
+                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved"):
     """Oracle of one static-cache step (VoxCPM page, 'What matches
     upstream', attention bullet, and 'Memory and speed', attention_span).
 
@@ -290,7 +315,7 @@ def mzref_decode(dtype: str, q_bits, k_bits, v_bits, *, span: int, mask=None,
         for h in range(Hq):
             qh = q[b, h]
             if rope_base > 0:
-                qh = rope_interleaved(qh, np.asarray(q_pos)[b], rope_base)
+                qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style)
             o[b, h], _ = attend(qh, k[b, h // G], v[b, h // G], live[b, h], scale)
     return o
 

@@ -201,6 +201,38 @@ def pin_causal_first_query_is_v0():
     _close(lse[0, :, 0], np.einsum("hd,hd->h", q[0, :, 0], k[0, :, 0]) / math.sqrt(8), 1e-12, "causal lse q0")
 
 
+def pin_rope_half_split_vs_transformers():
+    """Half-split pairing against transformers' Llama rotary helper
+    (``apply_rotary_pos_emb`` with ``rotate_half``; a library routine the
+    oracle does not call), in fp64, cos/sin built as that model family
+    builds them: the frequency vector repeated twice."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    rng = np.random.default_rng(23)
+    for D, base in ((8, 1e4), (64, 1e6), (128, 1e4)):
+        x, y = _rand(rng, 2, 3, 7, D), _rand(rng, 2, 3, 7, D)
+        pos = np.array([0, 1, 5, 77, 1000, 2047, 4095])
+        inv = 1.0 / (base ** (np.arange(0, D, 2, dtype=np.float64) / D))
+        emb = np.concatenate([np.outer(pos, inv)] * 2, axis=-1)
+        cos, sin = torch.from_numpy(np.cos(emb))[None], torch.from_numpy(np.sin(emb))[None]
+        rx, ry = apply_rotary_pos_emb(torch.from_numpy(x), torch.from_numpy(y), cos, sin)
+        _close(mzref.rope_half_split(x, pos, base), rx.numpy(), 1e-12, f"half split D{D} q")
+        _close(mzref.rope_half_split(y, pos, base), ry.numpy(), 1e-12, f"half split D{D} k")
+
+
+def pin_rope_styles_differ_by_permutation():
+    """The two pairings are one rotation seen through a fixed permutation of
+    the feature axis (even features first, then odd), so attention with
+    half-split RoPE equals attention with interleaved RoPE on permuted q/k."""
+    rng = np.random.default_rng(24)
+    B, H, S, D = 1, 2, 9, 16
+    q, k, v = _rand(rng, B, H, S, D), _rand(rng, B, H, S, D), _rand(rng, B, H, S, D)
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])  # interleaved -> half-split layout
+    inv = np.argsort(perm)
+    o_half, _ = mzref.mzref_fwd("f32", _bits64(q), _bits64(k), _bits64(v), rope_base=1e4, rope_style="half")
+    o_int, _ = mzref.mzref_fwd("f32", _bits64(q[..., inv]), _bits64(k[..., inv]), _bits64(v), rope_base=1e4)
+    _close(o_half, o_int, 1e-12, "styles by permutation")
+
+
 def pin_sdpa_no_mask():
     rng = np.random.default_rng(5)
     q, k, v = _rand(rng, 2, 4, 11, 32), _rand(rng, 2, 4, 19, 32), _rand(rng, 2, 4, 19, 32)
@@ -427,4 +459,5 @@ ALL_PINS = [
     pin_packed_equals_separate, pin_segment_positions, pin_segment_padding,
     pin_decode_vs_sdpa_truncated, pin_decode_span_invariance, pin_decode_rope_q,
     pin_sdpa_causal, pin_causal_first_query_is_v0,
+    pin_rope_half_split_vs_transformers, pin_rope_styles_differ_by_permutation,
 ]

@@ -19,7 +19,7 @@ MUTANTS = {
     "rope_sign": ("out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
     "rope_half_split": ("x0, x1 = x[..., 0::2], x[..., 1::2]", "x0, x1 = x[..., :D // 2], x[..., D // 2:]"),
     "rope_freq_no_2": ("np.power(float(base), -2.0 * i / head_dim)", "np.power(float(base), -1.0 * i / head_dim)"),
-    "rope_k_unrotated": ("kh = rope_interleaved(kh, pk[b], rope_base)", "kh = kh"),
+    "rope_k_unrotated": ("kh = rope(kh, pk[b], rope_base, rope_style)", "kh = kh"),
     "rope_partial_off_by_one": ("min(pe_attn_head, n_heads_q)", "min(pe_attn_head + 1, n_heads_q)"),
     "gqa_modulo": ("hk = h // G", "hk = h % Hkv"),
     "scale_inverted": ("if scale <= 0:\n        scale = 1.0 / math.sqrt(D)\n    n_rot",
@@ -36,11 +36,16 @@ MUTANTS = {
                                 "live = (sq[:, :, None] == sk[:, None, :])"),
     "segment_pos_no_restart": ("            start = i\n", "            pass\n"),
     "decode_span_inclusive": ("in_span = np.arange(C) < span", "in_span = np.arange(C) <= span"),
-    "decode_q_rope_dropped": ("qh = rope_interleaved(qh, np.asarray(q_pos)[b], rope_base)", "qh = qh"),
+    "decode_q_rope_dropped": ("qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style)", "qh = qh"),
     "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "fp16_bias": ("(e - 15)", "(e - 14)"),
     "fp16_subnormal": ("sub = np.ldexp(f, -24)", "sub = np.ldexp(f, -23)"),
     "empty_row_nan": ("o = np.zeros((q.shape[0], v.shape[1]))", "o = np.full((q.shape[0], v.shape[1]), np.nan)"),
+    "half_split_sign": ("out[..., :D // 2] = x0 * c - x1 * s", "out[..., :D // 2] = x0 * c + x1 * s"),
+    "half_split_as_interleaved": ("x0, x1 = x[..., :D // 2], x[..., D // 2:]",
+                                  "x0, x1 = x[..., 0::2], x[..., 1::2]"),
+    "half_split_style_ignored": ("    if style == \"half\":\n        return rope_half_split(x, pos, base)",
+                                 "    if style == \"half\":\n        return rope_interleaved(x, pos, base)"),
     "causal_strict": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                       "live = np.arange(Sk)[None, :] < np.arange(Sq)[:, None]"),
     "causal_bottom_right": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
