@@ -95,8 +95,12 @@ typedef enum mz_mask_kind {
  * head_dim: 64 or 128.  seq_q, seq_k: 0 .. 2^20.
  *
  * scale: <= 0 selects 1/sqrt(head_dim); otherwise used as given.
- * rope_base: 0 = no rotary embedding; > 0 rotates adjacent pairs
- *   (x[2i], x[2i+1]) of q and k by pos * rope_base^(-2i/head_dim).
+ * rope_base: 0 = no rotary embedding; > 0 rotates the pairs of q and k
+ *   chosen by rope_style by pos * rope_base^(-2i/head_dim), pair i.
+ * rope_style: 0 = interleaved, pair i is (x[2i], x[2i+1]) (F5-TTS page,
+ *   x-transformers style); 1 = half split, pair i is (x[i], x[i+D/2]) (the
+ *   "rotate half" layout of Llama-family models).  Other values:
+ *   MZ_ERR_VALUE.
  * pe_attn_head: < 0 rotates every head; n >= 0 rotates query heads 0..n-1
  *   and the K heads they read.  With GQA only "none" (0) or "all" (< 0 or
  *   >= heads_q) is accepted (MZ_ERR_UNSUPPORTED otherwise).
@@ -120,7 +124,7 @@ typedef struct mzattn_fwd_args {
   int32_t pe_attn_head;
   int32_t mask_kind;    /* mz_mask_kind */
   float scale;
-  int32_t reserved0;    /* must be 0 */
+  int32_t rope_style;   /* 0 interleaved, 1 half split */
   double rope_base;
   const void* q;
   const void* k;
@@ -184,7 +188,8 @@ int mzattn_validate_fwd(const mzattn_fwd_args* args);
  * query t of head h iff j < span and mask[b, h, t, j] != 0 (mask NULL =
  * every key in the span).  The cache holds keys already rotated; with
  * rope_base > 0 the queries are rotated at q_pos [batch, q_len] (int32,
- * batch stride q_pos_stride_b, required then).  q_len: 1 .. 16.
+ * batch stride q_pos_stride_b, required then), pairs chosen by rope_style
+ * as in mzattn_fwd_args.  q_len: 1 .. 16.
  * heads_q / heads_kv * q_len must not exceed 64.  head_dim: 64 or 128.
  *
  * The result does not depend on span beyond the last live key, bit for
@@ -205,6 +210,7 @@ typedef struct mzattn_decode_args {
   int32_t dtype;
   int32_t batch, heads_q, heads_kv, q_len, head_dim, cache_len, span;
   float scale;
+  int32_t rope_style;   /* 0 interleaved, 1 half split */
   double rope_base;
   const void* q;
   int64_t q_stride[3];

@@ -31,6 +31,13 @@ MZ_ERR_VALUE = -10
 
 MZ_F32, MZ_F16, MZ_BF16 = 0, 1, 2
 MZ_MASK_NONE, MZ_MASK_BOOL, MZ_MASK_SEGMENT, MZ_MASK_CAUSAL = 0, 1, 2, 3
+ROPE_STYLES = {"interleaved": 0, "half": 1}
+
+
+def _rope_style(style) -> int:
+    if style not in ROPE_STYLES:
+        raise MzattnError(MZ_ERR_VALUE, f"rope_style must be one of {sorted(ROPE_STYLES)}")
+    return ROPE_STYLES[style]
 
 _i64x3 = ctypes.c_int64 * 3
 _i64x4 = ctypes.c_int64 * 4
@@ -59,7 +66,7 @@ class FwdArgs(ctypes.Structure):
         ("pe_attn_head", ctypes.c_int32),
         ("mask_kind", ctypes.c_int32),
         ("scale", ctypes.c_float),
-        ("reserved0", ctypes.c_int32),
+        ("rope_style", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("q", ctypes.c_void_p),
         ("k", ctypes.c_void_p),
@@ -97,6 +104,7 @@ class DecodeArgs(ctypes.Structure):
         ("cache_len", ctypes.c_int32),
         ("span", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("rope_style", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("q", ctypes.c_void_p),
         ("q_stride", _i64x3),
@@ -252,6 +260,7 @@ class FwdCall:
 
     def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
+                 rope_style: str = "interleaved",
                  out=None, return_lse: bool = False, workspace=None, stream=None):
         torch = _torch()
         L = lib()
@@ -265,6 +274,7 @@ class FwdCall:
         a.pe_attn_head = pe_attn_head
         a.scale = float(scale)
         a.rope_base = float(rope_base)
+        a.rope_style = _rope_style(rope_style)
         o = out if out is not None else torch.empty(B, Hq, Sq, D, dtype=q.dtype, device=q.device)
         a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
         a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
@@ -343,6 +353,7 @@ class FwdCall:
 
 def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
+               rope_style: str = "interleaved",
                out=None, return_lse: bool = False, workspace=None, stream=None):
     """Masked bidirectional attention forward (see ``mzattn_fwd`` in
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
@@ -350,7 +361,7 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = Fal
     [B, S] (segment mode); causal: key j live for query i iff j <= i.
     Returns o (and lse when ``return_lse``)."""
     return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, causal=causal, pos_q=pos_q, pos_k=pos_k,
-                   scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, out=out,
+                   scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, out=out,
                    return_lse=return_lse, workspace=workspace, stream=stream)()
 
 
@@ -360,7 +371,7 @@ class DecodeCall:
     shape, strides and dtype; ``__call__`` launches on the call's stream."""
 
     def __init__(self, q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
-                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, out=None,
+                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved", out=None,
                  workspace=None, stream=None):
         torch = _torch()
         L = lib()
@@ -374,6 +385,7 @@ class DecodeCall:
         a.span = C if span is None else int(span)
         a.scale = float(scale)
         a.rope_base = float(rope_base)
+        a.rope_style = _rope_style(rope_style)
         o = out if out is not None else torch.empty(B, Hq, T, D, dtype=q.dtype, device=q.device)
         a.q, a.k_cache, a.v_cache, a.o = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr()
         a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k_cache, "k_cache")
@@ -412,11 +424,11 @@ class DecodeCall:
 
 
 def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
-                  scale: float = 0.0, rope_base: float = 0.0, q_pos=None, out=None,
-                  workspace=None, stream=None):
+                  scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
+                  out=None, workspace=None, stream=None):
     """One static-cache step (see ``mzattn_decode`` in include/mzattn.h).
     q [B, Hq, q_len, D]; k_cache / v_cache [B, Hkv, cache_len, D]; keys
     [0, span) considered (default: the whole cache); mask: bool
     [B|1, Hq|1, q_len|1, cache_len] or None."""
     return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
-                      q_pos=q_pos, out=out, workspace=workspace, stream=stream)()
+                      q_pos=q_pos, rope_style=rope_style, out=out, workspace=workspace, stream=stream)()

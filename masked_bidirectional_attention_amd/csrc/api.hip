@@ -71,7 +71,7 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
   if (a->struct_size != sizeof(mzattn_fwd_args))
     return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_fwd_args) %zu", a->struct_size,
                 sizeof(mzattn_fwd_args));
-  if (a->reserved0 != 0) return fail(MZ_ERR_ABI, "reserved0 must be 0");
+  if (a->rope_style != 0 && a->rope_style != 1) return fail(MZ_ERR_VALUE, "rope_style must be 0 or 1 (got %d)", a->rope_style);
   if (a->dtype != MZ_F32 && a->dtype != MZ_F16 && a->dtype != MZ_BF16)
     return fail(MZ_ERR_DTYPE, "unknown dtype %d", a->dtype);
   if (a->batch < 0 || a->batch > kMaxBatch) return fail(MZ_ERR_SHAPE, "batch %d outside [0, %d]", a->batch, kMaxBatch);
@@ -221,6 +221,8 @@ int plan_decode(const mzattn_decode_args* a, DecPlan* pl) {
   if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
   if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
     return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
+  if (a->rope_style != 0 && a->rope_style != 1)
+    return fail(MZ_ERR_VALUE, "rope_style must be 0 or 1 (got %d)", a->rope_style);
   pl->R = G * a->q_len;
   pl->n_chunks = a->span > 0 ? (a->span + mz::DEC_CHUNK - 1) / mz::DEC_CHUNK : 1;
   pl->n_chunks_max = a->cache_len > 0 ? (a->cache_len + mz::DEC_CHUNK - 1) / mz::DEC_CHUNK : 1;
@@ -293,6 +295,7 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   }
   char* ws = static_cast<char*>(a->workspace);
   p.n_rot = pl.n_rot; p.n_rot_kv = pl.n_rot_kv;
+  p.rope_style = a->rope_style;
   if (pl.n_rot > 0) {
     p.log2_base = log2(a->rope_base);
     p.rope_tab = reinterpret_cast<float2*>(ws + pl.off_tab);
@@ -429,6 +432,7 @@ int mzattn_decode(const mzattn_decode_args* a, void* stream) {
   char* ws = static_cast<char*>(a->workspace);
   if (a->rope_base > 0.0) {
     p.rope = 1;
+    p.rope_style = a->rope_style;
     p.log2_base = log2(a->rope_base);
     p.q_in = a->q;
     for (int i = 0; i < 3; ++i) p.q_in_s[i] = a->q_stride[i];

@@ -33,11 +33,20 @@ __global__ void decode_q_rotate16_kernel(const DecodeParams p) {
   const int h = (int)((row / p.T) % p.Hq);
   const int b = (int)(row / ((int64_t)p.T * p.Hq));
   const uint16_t* src = (const uint16_t*)p.q_in + b * p.q_in_s[0] + h * p.q_in_s[1] + (int64_t)t * p.q_in_s[2];
-  const uint32_t w = *(const uint32_t*)(src + 2 * i);
-  const float a = Elem<T>::to_f32((uint16_t)(w & 0xFFFF));
-  const float c = Elem<T>::to_f32((uint16_t)(w >> 16));
   const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
-  ((uint32_t*)p.q)[row * half + i] = Elem<T>::pack2(fmaf(a, cs.x, -c * cs.y), fmaf(c, cs.x, a * cs.y));
+  if (p.rope_style == 1) {
+    // half split: pair (i, i + D/2)
+    const float a = Elem<T>::to_f32(src[i]), c = Elem<T>::to_f32(src[i + half]);
+    const uint32_t r = Elem<T>::pack2(fmaf(a, cs.x, -c * cs.y), fmaf(c, cs.x, a * cs.y));
+    uint16_t* dst = (uint16_t*)p.q + row * p.D;
+    dst[i] = (uint16_t)(r & 0xFFFF);
+    dst[i + half] = (uint16_t)(r >> 16);
+  } else {
+    const uint32_t w = *(const uint32_t*)(src + 2 * i);
+    const float a = Elem<T>::to_f32((uint16_t)(w & 0xFFFF));
+    const float c = Elem<T>::to_f32((uint16_t)(w >> 16));
+    ((uint32_t*)p.q)[row * half + i] = Elem<T>::pack2(fmaf(a, cs.x, -c * cs.y), fmaf(c, cs.x, a * cs.y));
+  }
 }
 
 __global__ void decode_q_rotate32_kernel(const DecodeParams p) {
@@ -51,9 +60,13 @@ __global__ void decode_q_rotate32_kernel(const DecodeParams p) {
   const int h = (int)((row / p.T) % p.Hq);
   const int b = (int)(row / ((int64_t)p.T * p.Hq));
   const float* src = (const float*)p.q_in + b * p.q_in_s[0] + h * p.q_in_s[1] + (int64_t)t * p.q_in_s[2];
-  const float2 x = *(const float2*)(src + 2 * i);
+  // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
+  const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
+  const float2 x = make_float2(src[d0], src[d1]);
   const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
-  ((float2*)p.q)[row * half + i] = make_float2(fmaf(x.x, cs.x, -x.y * cs.y), fmaf(x.y, cs.x, x.x * cs.y));
+  float* dst = (float*)p.q + row * p.D;
+  dst[d0] = fmaf(x.x, cs.x, -x.y * cs.y);
+  dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
 }
 
 __device__ inline bool dec_live(const DecodeParams& p, int b, int kvh, int n, int key) {

@@ -169,10 +169,12 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
   return p.pos_q[b * p.pos_q_sb + i];
 }
 
-// One thread per 8 consecutive elements (4 pairs) of a K row.
-template <typename T>
+// One thread per 8 consecutive elements of a K row: 4 adjacent pairs
+// (interleaved), or with HALF 8 elements of the first half and their 8
+// partners D/2 further (half split).
+template <typename T, bool HALF>
 __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
-  const int q8 = p.D / 8;
+  const int q8 = HALF ? p.D / 16 : p.D / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
   if (idx >= nrows * q8) return;
@@ -182,9 +184,31 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int hk = (int)((row / p.Sk) % p.n_rot_kv);
   const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
   const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + d0;
-  const uint4 x = *(const uint4*)src;
-  const uint4 r = rope_quad<T>(x, p.rope_tab, p.rope_tab_len, key_position(p, b, j), d0, p.D, p.log2_base);
-  *(uint4*)((uint16_t*)p.k_rot + row * p.D + d0) = r;
+  uint16_t* dst = (uint16_t*)p.k_rot + row * p.D + d0;
+  const int pos = key_position(p, b, j);
+  if constexpr (!HALF) {
+    *(uint4*)dst = rope_quad<T>(*(const uint4*)src, p.rope_tab, p.rope_tab_len, pos, d0, p.D, p.log2_base);
+  } else {
+    const int hd = p.D / 2;
+    const uint4 x0 = *(const uint4*)src, x1 = *(const uint4*)(src + hd);
+    uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float r[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
+        const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
+        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, d0 + 2 * t + e, p.D, p.log2_base);
+        r[0][e] = fmaf(a, cs.x, -c * cs.y);
+        r[1][e] = fmaf(c, cs.x, a * cs.y);
+      }
+      lo[t] = Elem<T>::pack2(r[0][0], r[0][1]);
+      hi[t] = Elem<T>::pack2(r[1][0], r[1][1]);
+    }
+    *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *(uint4*)(dst + hd) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
 }
 
 __global__ void k_rotate32_kernel(const FwdParams p) {
@@ -197,13 +221,14 @@ __global__ void k_rotate32_kernel(const FwdParams p) {
   const int j = (int)(row % p.Sk);
   const int hk = (int)((row / p.Sk) % p.n_rot_kv);
   const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
-  const float* src = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + 2 * i;
-  const float2 x = *(const float2*)src;
+  // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
+  const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
+  const float* src = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2];
+  const float2 x = make_float2(src[d0], src[d1]);
   const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.log2_base);
-  float2 r;
-  r.x = fmaf(x.x, cs.x, -x.y * cs.y);
-  r.y = fmaf(x.y, cs.x, x.x * cs.y);
-  ((float2*)p.k_rot)[row * half + i] = r;
+  float* dst = (float*)p.k_rot + row * p.D;
+  dst[d0] = fmaf(x.x, cs.x, -x.y * cs.y);
+  dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,11 +367,36 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
     const float sc = p.scale_log2;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (qvalid) {
-        x = *(const uint4*)(qrow + s * 16 + hh * 8);
-        uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+    for (int s = 0; s < NS; ++s) qf[s] = qvalid ? *(const uint4*)(qrow + s * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+    if (qvalid && rot && p.rope_style == 1) {
+      // half split: element e of chunk s pairs with element e of chunk
+      // s + NS/2 (d and d + D/2), both held by this lane
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s) {
+        uint32_t lo[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
+        uint32_t hi[4] = {qf[s + NS / 2].x, qf[s + NS / 2].y, qf[s + NS / 2].z, qf[s + NS / 2].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float r[2][2];  // [first half, second half][element 2t, 2t + 1]
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
+            const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
+            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8 + 2 * t + e, D, p.log2_base);
+            r[0][e] = fmaf(a, cs.x, -c * cs.y);
+            r[1][e] = fmaf(c, cs.x, a * cs.y);
+          }
+          lo[t] = Elem<T>::pack2(r[0][0] * sc, r[0][1] * sc);
+          hi[t] = Elem<T>::pack2(r[1][0] * sc, r[1][1] * sc);
+        }
+        qf[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        qf[s + NS / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    } else if (qvalid) {
+      // interleaved: the pairs are the two halves of each 32-bit word
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
         const int d0 = s * 16 + hh * 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -361,9 +411,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           }
           wv[t] = Elem<T>::pack2(a * sc, c * sc);
         }
-        x = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        qf[s] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
-      qf[s] = x;
     }
   }
 
@@ -886,16 +935,19 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
     const float* qrow = (const float*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
     const bool rot = h < p.n_rot;
     const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
+    // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
+    const bool half = p.rope_style == 1;
     for (int i = 0; i < D / 2; ++i) {
-      float2 x = qvalid ? *(const float2*)(qrow + 2 * i) : make_float2(0.f, 0.f);
+      const int d0 = half ? i : 2 * i, d1 = half ? i + D / 2 : 2 * i + 1;
+      float2 x = qvalid ? make_float2(qrow[d0], qrow[d1]) : make_float2(0.f, 0.f);
       if (rot && qvalid) {
         const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, i, D, p.log2_base);
         const float a = fmaf(x.x, cs.x, -x.y * cs.y);
         const float c = fmaf(x.y, cs.x, x.x * cs.y);
         x = make_float2(a, c);
       }
-      Qs[lane][2 * i] = x.x * p.scale_log2;
-      Qs[lane][2 * i + 1] = x.y * p.scale_log2;
+      Qs[lane][d0] = x.x * p.scale_log2;
+      Qs[lane][d1] = x.y * p.scale_log2;
     }
   }
   const float* kbase;
@@ -1022,9 +1074,15 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
       const unsigned nblk = (unsigned)((nrows + rows_per_blk - 1) / rows_per_blk);
       k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
     } else {
-      const unsigned nblk = (unsigned)((nrows * (p.D / 8) + 255) / 256);
-      if (p.dtype == 2) k_rotate16_kernel<BF16><<<dim3(nblk), dim3(256), 0, s>>>(p);
-      else k_rotate16_kernel<F16><<<dim3(nblk), dim3(256), 0, s>>>(p);
+      const bool half = p.rope_style == 1;
+      const unsigned nblk = (unsigned)((nrows * (p.D / (half ? 16 : 8)) + 255) / 256);
+      if (p.dtype == 2) {
+        if (half) k_rotate16_kernel<BF16, true><<<dim3(nblk), dim3(256), 0, s>>>(p);
+        else k_rotate16_kernel<BF16, false><<<dim3(nblk), dim3(256), 0, s>>>(p);
+      } else {
+        if (half) k_rotate16_kernel<F16, true><<<dim3(nblk), dim3(256), 0, s>>>(p);
+        else k_rotate16_kernel<F16, false><<<dim3(nblk), dim3(256), 0, s>>>(p);
+      }
     }
   }
   return hipGetLastError();

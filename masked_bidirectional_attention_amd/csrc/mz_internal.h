@@ -30,6 +30,7 @@ struct FwdParams {
   int64_t qs[3], ks[3], vs[3], os[3];
   // rotary embedding
   int n_rot, n_rot_kv;
+  int rope_style;  // 0 interleaved (2i, 2i+1), 1 half split (i, i + D/2)
   double log2_base;
   int pos_q_mode, pos_k_mode;
   const int32_t* pos_q;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
@@ -81,6 +82,7 @@ struct DecodeParams {
   int64_t q_pos_sb;
   double log2_base;
   int rope;
+  int rope_style;  // 0 interleaved, 1 half split
   // workspace
   float2* part_ml;     // [B][Hkv][n_chunks][R]   (m in log2 units, l)
   float* part_acc;     // [B][Hkv][n_chunks][R][D]

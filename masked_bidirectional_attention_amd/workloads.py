@@ -61,6 +61,7 @@ class FwdCase:
     scale: float = 0.0          # <= 0 means 1/sqrt(D)
     rope_base: float = 0.0      # 0 means no RoPE
     pe_attn_head: int = -1      # < 0 means all heads
+    rope_style: str = "interleaved"  # or "half" (pairs (i, i + D/2))
     mask_kind: str = MASK_NONE
     mask: Optional[torch.Tensor] = None
     seg_q: Optional[torch.Tensor] = None
@@ -94,6 +95,7 @@ class DecodeCase:
     rope_base: float = 0.0
     q_pos: Optional[torch.Tensor] = None
     filled: int = 0             # informational: number of filled cache rows
+    rope_style: str = "interleaved"
 
 
 def _randn(gen: torch.Generator, shape, dtype: str, mult: float = 1.0) -> torch.Tensor:

@@ -21,7 +21,7 @@ def run_fwd(case: W.FwdCase, return_lse=False, q=None, k=None, v=None):
     k = dev(case.k) if k is None else k
     v = dev(case.v) if v is None else v
     kw = dict(scale=case.scale, rope_base=case.rope_base, pe_attn_head=case.pe_attn_head,
-              pos_q=dev(case.pos_q), pos_k=dev(case.pos_k), return_lse=return_lse)
+              rope_style=case.rope_style, pos_q=dev(case.pos_q), pos_k=dev(case.pos_k), return_lse=return_lse)
     if case.mask_kind == W.MASK_BOOL:
         kw["mask"] = dev(case.mask)
     elif case.mask_kind == W.MASK_SEGMENT:
@@ -41,14 +41,15 @@ def oracle_fwd(case: W.FwdCase, heads=None):
         pos_k=None if case.pos_k is None else case.pos_k.numpy(),
         mask_kind=case.mask_kind, mask=None if case.mask is None else case.mask.numpy(),
         seg_q=None if case.seg_q is None else case.seg_q.numpy(),
-        seg_k=None if case.seg_k is None else case.seg_k.numpy(), heads=heads)
+        seg_k=None if case.seg_k is None else case.seg_k.numpy(), heads=heads, rope_style=case.rope_style)
 
 
 def run_decode(case: W.DecodeCase, span=None, k=None, v=None):
     o = mz.mzattn_decode(dev(case.q), dev(case.k_cache) if k is None else k,
                          dev(case.v_cache) if v is None else v,
                          span=case.span if span is None else span, mask=dev(case.mask),
-                         scale=case.scale, rope_base=case.rope_base, q_pos=dev(case.q_pos))
+                         scale=case.scale, rope_base=case.rope_base, q_pos=dev(case.q_pos),
+                         rope_style=case.rope_style)
     torch.cuda.synchronize()
     return o
 
@@ -58,7 +59,8 @@ def oracle_decode(case: W.DecodeCase, span=None):
         case.dtype, W.to_bits(case.q), W.to_bits(case.k_cache), W.to_bits(case.v_cache),
         span=case.span if span is None else span,
         mask=None if case.mask is None else case.mask.numpy(), scale=case.scale,
-        rope_base=case.rope_base, q_pos=None if case.q_pos is None else case.q_pos.numpy())
+        rope_base=case.rope_base, q_pos=None if case.q_pos is None else case.q_pos.numpy(),
+        rope_style=case.rope_style)
 
 
 def to64(t: torch.Tensor) -> np.ndarray:

@@ -170,7 +170,7 @@ def fwd_cases():
 
     return [
         ("struct_size", mutate("struct_size", 12), B.MZ_ERR_ABI),
-        ("reserved0", mutate("reserved0", 3), B.MZ_ERR_ABI),
+        ("rope_style", mutate("rope_style", 3), B.MZ_ERR_VALUE),
         ("dtype", mutate("dtype", 7), B.MZ_ERR_DTYPE),
         ("batch<0", mutate("batch", -1), B.MZ_ERR_SHAPE),
         ("heads_q=0", mutate("heads_q", 0), B.MZ_ERR_SHAPE),
@@ -296,6 +296,7 @@ def dec_cases():
         ("gqa_ratio", mutate("heads_kv", 3), B.MZ_ERR_SHAPE),
         ("q_len0", mutate("q_len", 0), B.MZ_ERR_SHAPE),
         ("q_len17", mutate("q_len", 17), B.MZ_ERR_SHAPE),
+        ("rope_style", mutate("rope_style", 2), B.MZ_ERR_VALUE),
         ("head_dim", mutate("head_dim", 256), B.MZ_ERR_UNSUPPORTED),
         ("span_big", mutate("span", 8193), B.MZ_ERR_VALUE),
         ("span_neg", mutate("span", -1), B.MZ_ERR_VALUE),

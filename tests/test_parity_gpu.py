@@ -205,6 +205,46 @@ def test_causal_equals_bool_tril():
     assert torch.equal(a, b)
 
 
+HALF_SHAPES = [
+    (1, 4, 4, 100, 140, 64),
+    (2, 8, 2, 257, 300, 128),
+    (1, 16, 2, 129, 129, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", HALF_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["none", "segment", "causal", "bool_key"])
+def test_rope_half_split(dtype, shape, kind):
+    """Half-split RoPE pairs (x_i, x_i+D/2) on q and k, against the oracle,
+    with explicit positions for the plain kind, derived ones for segments."""
+    B, Hq, Hkv, Sq, Sk, D = shape
+    seed = zlib.crc32(repr(("half", dtype, shape, kind)).encode()) % 10000
+    if kind == "segment":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sq, D, dtype, W.MASK_SEGMENT, rope_base=1e4, n_segments=3)
+    elif kind == "causal":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_CAUSAL, rope_base=1e6)
+    elif kind == "bool_key":
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_BOOL, mask_shape="key", rope_base=1e4,
+                            pe_attn_head=-1 if Hq != Hkv else 1)
+    else:
+        case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_NONE, rope_base=1e4, explicit_pos=True)
+    case.rope_style = "half"
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity(dtype, o, ref, f"{case.name} {shape} half")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_rope_half_split(dtype, D):
+    """Decode with half-split q rotation at q_pos."""
+    case = W.random_decode(41 + D, 2, 8, 2, 3, 700, D, dtype, filled=600, span=640, rope_base=1e4)
+    case.rope_style = "half"
+    o = run_decode(case)
+    assert_parity(dtype, o, oracle_decode(case), f"decode half D{D}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_explicit_positions(dtype):
     case = W.random_fwd(11, 2, 4, 4, 100, 140, 64, dtype, W.MASK_NONE, rope_base=1e4, explicit_pos=True)
