@@ -203,6 +203,7 @@ __global__ __launch_bounds__(256) void decode_merge32_kernel(const DecodeParams 
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int AS = D + 4;        // LDS row stride of the parked acc blocks (floats)
   constexpr int NS = D / 32;       // k-steps of K Q^T
   constexpr int NDB = D / 16;      // 16-row d blocks of O^T
   constexpr int VSD = D + 16;      // LDS row stride of V (elements)
@@ -213,7 +214,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   __shared__ __attribute__((aligned(16))) uint16_t Vs[4][32 * VSD];
   __shared__ float red_m[4][RP];
   __shared__ float red_l[4][RP];
-  static_assert(sizeof(float) * RP * D <= sizeof(uint16_t) * 4 * 32 * VSD, "acc fold reuses the V region");
+  __shared__ uint8_t live_s[RP][DEC_CHUNK];
+  static_assert(sizeof(float) * RP * AS <= sizeof(uint16_t) * 4 * 32 * VSD, "acc fold reuses the V region");
   float* acc_lds = reinterpret_cast<float*>(&Vs[0][0]);
 
   const int w = blockIdx.x;
@@ -228,67 +230,83 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const uint16_t* vbase = (const uint16_t*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
   // ---- a chunk in which no (row, key) pair is live is the identity of the
-  // merge: found from the mask alone, its K/V are never read
-  if (p.mask != nullptr) {
+  // merge: found from the mask alone, its K/V are never read.  The scan
+  // keeps the chunk's liveness bytes in LDS (one row when the mask is
+  // broadcast over heads and queries) for the score test below, so no mask
+  // load sits among the K/V loads.
+  const bool bcast = p.mask != nullptr && p.ms[1] == 0 && p.ms[2] == 0;
+  // (an empty span has one chunk and no key index valid to load)
+  bool dead = p.span <= 0;
+  if (p.mask != nullptr && !dead) {
     const int ckey0 = c * DEC_CHUNK;
-    // rows that share mask bytes (broadcast over heads and queries) are
-    // scanned once
-    const int rows = (p.ms[1] == 0 && p.ms[2] == 0) ? 1 : p.R;
+    const int rows = bcast ? 1 : p.R;
     bool any = false;
-    for (int idx = tid; idx < rows * DEC_CHUNK; idx += 256)
-      any |= dec_live(p, b, kvh, idx / DEC_CHUNK, ckey0 + idx % DEC_CHUNK);
-    if (!__syncthreads_or(any)) {
-      const int64_t pb = ((int64_t)unit * p.n_chunks + c) * p.R;
-      for (int idx = tid; idx < p.R * (D / 4); idx += 256)
-        *(float4*)(p.part_acc + (pb + idx / (D / 4)) * D + (idx % (D / 4)) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int n = tid; n < p.R; n += 256) p.part_ml[pb + n] = make_float2(0.f, 0.f);
-      return;
+    for (int idx = tid; idx < rows * DEC_CHUNK; idx += 256) {
+      const bool lv = dec_live(p, b, kvh, idx / DEC_CHUNK, ckey0 + idx % DEC_CHUNK);
+      live_s[idx / DEC_CHUNK][idx % DEC_CHUNK] = lv;
+      any |= lv;
     }
+    dead = !__syncthreads_or(any);
+  }
+  if (dead) {
+    const int64_t pb = ((int64_t)unit * p.n_chunks + c) * p.R;
+    for (int idx = tid; idx < p.R * (D / 4); idx += 256)
+      *(float4*)(p.part_acc + (pb + idx / (D / 4)) * D + (idx % (D / 4)) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int n = tid; n < p.R; n += 256) p.part_ml[pb + n] = make_float2(0.f, 0.f);
+    return;
   }
 
-  // ---- issue every global load of this wave up front
-  uint4 kf[2][NS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = key0 + kb * 16 + l16;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kf[kb][s] = key < p.span ? *(const uint4*)(kbase + (int64_t)key * p.ks[2] + s * 32 + g4 * 8)
-                               : make_uint4(0, 0, 0, 0);
-  }
-  uint4 vr[NVL];
+  // ---- issue every global load of this wave up front, unconditionally:
+  // keys past the span read row span - 1 and rows past R read row R - 1
+  // (in bounds; their scores are masked to -inf below, so their weights
+  // are exact zeros).  Conditional loads would each end in a wait, making
+  // the loads one dependent round trip after another.
+  const int klast = p.span - 1;
+  u32x4_t vr[NVL];  // a native vector type: one load each, kept in registers
 #pragma unroll
   for (int it = 0; it < NVL; ++it) {
     const int r = it * RPI + lane / CH, cc = lane % CH;
-    const int key = key0 + r;
-    vr[it] = key < p.span ? *(const uint4*)(vbase + (int64_t)key * p.vs[2] + cc * 8) : make_uint4(0, 0, 0, 0);
+    const int key = min(key0 + r, klast);
+    vr[it] = *(const u32x4_t*)(vbase + (int64_t)key * p.vs[2] + cc * 8);
+  }
+  uint4 kf[2][NS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = min(key0 + kb * 16 + l16, klast);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[kb][s] = *(const uint4*)(kbase + (int64_t)key * p.ks[2] + s * 32 + g4 * 8);
   }
   uint4 qf[NB][NS];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n = nb * 16 + l16;
+    const int n = min(nb * 16 + l16, p.R - 1);
     const int g = n / p.T, t = n % p.T;
     const int h = kvh * p.G + g;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      qf[nb][s] = n < p.R ? *(const uint4*)((const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] +
-                                            (int64_t)t * p.qs[2] + s * 32 + g4 * 8)
-                          : make_uint4(0, 0, 0, 0);
+      qf[nb][s] = *(const uint4*)((const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t * p.qs[2] + s * 32 +
+                                  g4 * 8);
   }
-  // liveness of this lane's score elements (mask loads overlap the K/V loads)
+  // every load above is issued before the first use of any of them (the
+  // scheduler would otherwise start the V loads after the K.Q MFMAs)
+  asm volatile("" ::: "memory");
+  // liveness of this lane's score elements (mask bytes from the scan)
   bool live[2][NB][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        live[kb][nb][v] = dec_live(p, b, kvh, nb * 16 + l16, key0 + kb * 16 + g4 * 4 + v);
+      for (int v = 0; v < 4; ++v) {
+        const int n = nb * 16 + l16, j = wave * 32 + kb * 16 + g4 * 4 + v;
+        const bool in = n < p.R && c * DEC_CHUNK + j < p.span;
+        live[kb][nb][v] = in && (p.mask == nullptr || live_s[bcast ? 0 : n][j] != 0);
+      }
   // V rows into this wave's LDS region
 #pragma unroll
   for (int it = 0; it < NVL; ++it) {
     const int r = it * RPI + lane / CH, cc = lane % CH;
-    *(uint4*)&Vs[wave][r * VSD + cc * 8] = vr[it];
+    *(u32x4_t*)&Vs[wave][r * VSD + cc * 8] = vr[it];
   }
 
   // ---- scores S^T (keys x rows), masked, in the log2 domain
@@ -364,23 +382,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   // every wave has finished reading it) and write the chunk partial
   __syncthreads();
   const int64_t pbase = ((int64_t)unit * p.n_chunks + c) * p.R;
-  if constexpr (sizeof(float) * 4 * RP * D <= sizeof(uint16_t) * 4 * 32 * VSD) {
+  // (rows AS = D + 4 floats apart: the 16 rows one 16-byte store
+  // instruction touches then fall on distinct banks)
+  if constexpr (sizeof(float) * 4 * RP * AS <= sizeof(uint16_t) * 4 * 32 * VSD) {
     // every wave parks its block in its own region; then all threads add
     // the four in wave order
-    float* const own = acc_lds + wave * (RP * D);
+    float* const own = acc_lds + wave * (RP * AS);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) own[(nb * 16 + l16) * D + db * 16 + g4 * 4 + v] = oacc[nb][db][v];
+        *(f32x4_t*)&own[(nb * 16 + l16) * AS + db * 16 + g4 * 4] = oacc[nb][db];
     __syncthreads();
     for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
       const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
-      float4 x = *(const float4*)&acc_lds[n * D + d];
+      float4 x = *(const float4*)&acc_lds[n * AS + d];
 #pragma unroll
       for (int wv = 1; wv < 4; ++wv) {
-        const float4 y = *(const float4*)&acc_lds[wv * (RP * D) + n * D + d];
+        const float4 y = *(const float4*)&acc_lds[wv * (RP * AS) + n * AS + d];
         x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
       }
       *(float4*)(p.part_acc + (pbase + n) * D + d) = x;
@@ -395,7 +414,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              float* slot = &acc_lds[(nb * 16 + l16) * D + db * 16 + g4 * 4 + v];
+              float* slot = &acc_lds[(nb * 16 + l16) * AS + db * 16 + g4 * 4 + v];
               *slot = step == 0 ? oacc[nb][db][v] : *slot + oacc[nb][db][v];
             }
       }
@@ -403,7 +422,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     }
     for (int idx = tid; idx < p.R * (D / 4); idx += 256) {
       const int n = idx / (D / 4), d = (idx % (D / 4)) * 4;
-      *(float4*)(p.part_acc + (pbase + n) * D + d) = *(const float4*)&acc_lds[n * D + d];
+      *(float4*)(p.part_acc + (pbase + n) * D + d) = *(const float4*)&acc_lds[n * AS + d];
     }
   }
   for (int n = tid; n < p.R; n += 256) {

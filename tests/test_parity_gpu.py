@@ -399,3 +399,49 @@ def test_decode_call_set_cache():
     ref = mzref.mzref_decode("bf16", W.to_bits(a.q), W.to_bits(b2.k_cache), W.to_bits(b2.v_cache), span=500,
                              mask=a.mask.numpy())
     assert_parity("bf16", o2, ref, "decode after set_cache")
+
+
+# --------------------------------------------------------------------------
+# decode: no mask, empty span, 64 rows per head group; one workspace shared
+# by calls of several shapes and spans
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, q_len, cache, D, span   (no mask: every key in the span)
+    (2, 16, 2, 1, 8192, 128, 8192),
+    (1, 32, 2, 4, 1200, 128, 1100),   # 64 rows per head group
+    (2, 8, 1, 2, 700, 64, 513),
+    (1, 4, 4, 1, 300, 64, 1),
+    (1, 4, 2, 1, 300, 128, 0),        # empty span, no mask: output 0
+], ids=lambda s: "x".join(map(str, s)))
+def test_decode_no_mask(dtype, shape):
+    B, Hq, Hkv, T, C, D, span = shape
+    case = W.random_decode(zlib.crc32(repr(("nomask", dtype, shape)).encode()) % 10000, B, Hq, Hkv, T, C, D,
+                           dtype, C, span)
+    case.mask = None
+    o = run_decode(case)
+    if span == 0:
+        assert torch.all(o == 0)
+        return
+    assert_parity(dtype, o, oracle_decode(case), f"decode no mask {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_repeated_calls_share_workspace(dtype):
+    """Calls of several shapes and spans through one workspace that starts
+    as all-ones bytes (NaN as floats), each checked against the oracle:
+    nothing a call reads from the workspace may be left from before it."""
+    import masked_bidirectional_attention_amd as mz
+    cases = [W.random_decode(60 + i, B, Hq, Hkv, 1, C, 128, dtype, fill, span)
+             for i, (B, Hq, Hkv, C, fill, span) in enumerate([
+                 (2, 16, 2, 4096, 3000, 4096), (2, 16, 2, 4096, 3000, 3072), (1, 8, 1, 4096, 200, 256),
+                 (2, 16, 2, 4096, 4096, 4096), (2, 16, 2, 4096, 3000, 4096)])]
+    ws = torch.full((16 << 20,), 255, dtype=torch.uint8, device=dev(torch.zeros(1)).device)
+    for rep in range(2):
+        for c in cases:
+            call = mz.DecodeCall(dev(c.q), dev(c.k_cache), dev(c.v_cache), span=c.span, mask=dev(c.mask),
+                                 workspace=ws)
+            o = call()
+            torch.cuda.synchronize()
+            assert_parity(dtype, o, oracle_decode(c), f"{c.name} span={c.span} pass {rep}")
