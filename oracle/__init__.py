@@ -11,6 +11,7 @@ from .mzref import (  # noqa: F401
     decode_fp32,
     live_set_fwd,
     mzref_decode,
+    mzref_decode_append,
     mzref_fwd,
     parity_stats,
     rope_interleaved,

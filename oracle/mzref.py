@@ -320,6 +320,63 @@ def mzref_decode(dtype: str, q_bits, k_bits, v_bits, *, span: int, mask=None,
     return o
 
 
+def mzref_decode_append(dtype: str, q_bits, k_new_bits, v_new_bits, k_cache_bits, v_cache_bits, lens, *,
+                        mask=None, scale: float = 0.0, rope_base: float = 0.0, rope_style: str = "interleaved"):
+    """Oracle of one generation step that appends its own keys and values
+    to the static cache and reads the filled length from the cache state
+    instead of the host (VoxCPM page, 'Memory and speed': every patch waits
+    on the device for the language models' positions, copied from Python
+    integers, and CUDA graphs attend over the whole cache; 'What matches
+    upstream', attention bullet: the step attends to the static cache under
+    an explicit boolean mask, past the current length zero and masked).
+
+    Reading: the q_len new tokens of row b take cache rows and positions
+    lens[b] + t (t = 0 .. q_len-1); their keys are rotated at that position
+    (the cache stores rotated keys) and, with the values, written into the
+    cache; query t rotated at the same position attends to keys
+    j <= lens[b] + t (the filled rows and the new tokens up to itself),
+    further restricted by mask[b, h, t, j] when a mask is given.  A row with
+    lens[b] < 0 or lens[b] + q_len > cache_len overflows: nothing is
+    written and its output is 0.
+
+    q_bits [B, Hq, T, D], k_new_bits / v_new_bits [B, Hkv, T, D] (keys not
+    rotated), k_cache_bits / v_cache_bits [B, Hkv, C, D].  Returns
+    (o [B, Hq, T, D] fp64, k_rows [B, Hkv, T, D] fp64 (the rotated new
+    keys, unrounded), overflow [B] bool)."""
+    q = decode(q_bits, dtype)
+    kn = decode(k_new_bits, dtype)
+    vn = decode(v_new_bits, dtype)
+    k = decode(k_cache_bits, dtype).copy()
+    v = decode(v_cache_bits, dtype).copy()
+    B, Hq, T, D = q.shape
+    Hkv, C = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    if scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    lens = np.asarray(lens, dtype=np.int64)
+    o = np.zeros((B, Hq, T, D))
+    k_rows = np.zeros((B, Hkv, T, D))
+    overflow = np.zeros(B, dtype=bool)
+    m = np.ones((1, 1, 1, C), dtype=bool) if mask is None else np.asarray(mask, dtype=bool)
+    m = np.broadcast_to(m, (B, Hq, T, C))
+    for b in range(B):
+        L = int(lens[b])
+        if L < 0 or L + T > C:
+            overflow[b] = True
+            continue
+        pos = L + np.arange(T)
+        for hk in range(Hkv):
+            kr = rope(kn[b, hk], pos, rope_base, rope_style) if rope_base > 0 else kn[b, hk]
+            k_rows[b, hk] = kr
+            k[b, hk, L:L + T] = kr
+            v[b, hk, L:L + T] = vn[b, hk]
+        causal = np.arange(C)[None, :] <= pos[:, None]          # [T, C]
+        for h in range(Hq):
+            qh = rope(q[b, h], pos, rope_base, rope_style) if rope_base > 0 else q[b, h]
+            o[b, h], _ = attend(qh, k[b, h // G], v[b, h // G], causal & m[b, h], scale)
+    return o, k_rows, overflow
+
+
 # --------------------------------------------------------------------------
 # Comparison helpers (the tolerances the GPU path is held to)
 # --------------------------------------------------------------------------

@@ -451,6 +451,90 @@ def pin_decode_rope_q():
     _close(o, ref, 1e-12, "decode rope")
 
 
+def _rope_complex(x, pos, base):
+    """Interleaved rotation as complex multiplication (test-side, written
+    from the definition; x [..., S, D], pos [S])."""
+    D = x.shape[-1]
+    theta = 1.0 / (base ** (np.arange(0, D, 2, dtype=np.float64) / D))
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * np.asarray(pos, dtype=np.float64)[:, None] * theta)
+    out = np.empty_like(x)
+    out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+def pin_append_empty_cache_is_causal_sdpa():
+    """Appending q_len tokens to an empty cache (len 0) is causal attention
+    over the new tokens: torch SDPA is_causal (GQA) over q and k rotated at
+    positions 0 .. q_len-1 (complex form); the rows written are those
+    rotated keys."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, T, C, D = 2, 4, 2, 5, 40, 16
+    q, kn, vn = _rand(rng, B, Hq, T, D), _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D)
+    kc, vc = _rand(rng, B, Hkv, C, D), _rand(rng, B, Hkv, C, D)   # junk past the filled rows
+    o, k_rows, ovf = mzref.mzref_decode_append("f32", _bits64(q), _bits64(kn), _bits64(vn), _bits64(kc),
+                                               _bits64(vc), [0, 0], rope_base=1e4)
+    pos = np.arange(T)
+    qr, kr = _rope_complex(q, pos, 1e4), _rope_complex(kn, pos, 1e4)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (qr, kr, vn))
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True).numpy()
+    _close(o, ref, 1e-12, "append on empty cache")
+    _close(k_rows, kr, 1e-12, "appended key rows")
+    assert not ovf.any()
+
+
+def pin_append_single_token_first_row():
+    """One new token on an empty cache is the only live key of its query:
+    the output is its value exactly (p = 1, l = 1)."""
+    rng = np.random.default_rng(32)
+    q, kn, vn = _rand(rng, 1, 4, 1, 8), _rand(rng, 1, 2, 1, 8), _rand(rng, 1, 2, 1, 8)
+    kc, vc = _rand(rng, 1, 2, 20, 8), _rand(rng, 1, 2, 20, 8)
+    o, _, _ = mzref.mzref_decode_append("f32", _bits64(q), _bits64(kn), _bits64(vn), _bits64(kc), _bits64(vc),
+                                        [0], rope_base=1e4)
+    assert np.array_equal(o[0, :, 0], np.repeat(vn[0, :, 0], 2, axis=0))
+
+
+def pin_append_equals_sdpa_on_updated_cache():
+    """Rows of different filled lengths with a user mask: equals SDPA (GQA)
+    with the bool mask (j <= len + t) & mask over a cache whose rows
+    len .. len+T-1 hold the new keys rotated at those positions (complex
+    form) and the new values."""
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, T, C, D = 3, 6, 2, 3, 50, 16
+    lens = np.array([0, 17, 47])
+    q, kn, vn = _rand(rng, B, Hq, T, D), _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D)
+    kc, vc = _rand(rng, B, Hkv, C, D), _rand(rng, B, Hkv, C, D)
+    um = rng.random((B, Hq, T, C)) < 0.7
+    for b in range(B):
+        for t in range(T):
+            um[b, :, t, lens[b] + t] = True
+    o, _, ovf = mzref.mzref_decode_append("f32", _bits64(q), _bits64(kn), _bits64(vn), _bits64(kc), _bits64(vc),
+                                          lens, mask=um, rope_base=1e4)
+    assert not ovf.any()
+    k2, v2 = kc.copy(), vc.copy()
+    qr = np.empty_like(q)
+    live = np.zeros((B, Hq, T, C), dtype=bool)
+    for b in range(B):
+        pos = lens[b] + np.arange(T)
+        k2[b, :, lens[b]:lens[b] + T] = _rope_complex(kn[b], pos, 1e4)
+        v2[b, :, lens[b]:lens[b] + T] = vn[b]
+        qr[b] = _rope_complex(q[b], pos, 1e4)
+        live[b] = um[b] & (np.arange(C)[None, None, :] <= pos[None, :, None])
+    _close(o, _sdpa(qr, k2, v2, live, gqa=True), 1e-12, "append vs SDPA on the updated cache")
+
+
+def pin_append_overflow():
+    """A row whose new tokens would run past the cache end writes nothing
+    and gives 0; the last row that fits is computed."""
+    rng = np.random.default_rng(34)
+    T, C = 2, 10
+    q, kn, vn = _rand(rng, 2, 2, T, 8), _rand(rng, 2, 1, T, 8), _rand(rng, 2, 1, T, 8)
+    kc, vc = _rand(rng, 2, 1, C, 8), _rand(rng, 2, 1, C, 8)
+    o, _, ovf = mzref.mzref_decode_append("f32", _bits64(q), _bits64(kn), _bits64(vn), _bits64(kc), _bits64(vc),
+                                          [C - T, C - T + 1])
+    assert list(ovf) == [False, True]
+    assert np.all(o[1] == 0) and np.all(np.abs(o[0]) > 0)
+
+
 ALL_PINS = [
     pin_fp16_decode, pin_bf16_decode, pin_fp32_decode,
     pin_rope_complex_form, pin_rope_hand_values, pin_rope_properties,
@@ -460,4 +544,6 @@ ALL_PINS = [
     pin_decode_vs_sdpa_truncated, pin_decode_span_invariance, pin_decode_rope_q,
     pin_sdpa_causal, pin_causal_first_query_is_v0,
     pin_rope_half_split_vs_transformers, pin_rope_styles_differ_by_permutation,
+    pin_append_empty_cache_is_causal_sdpa, pin_append_single_token_first_row,
+    pin_append_equals_sdpa_on_updated_cache, pin_append_overflow,
 ]

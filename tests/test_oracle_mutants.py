@@ -50,6 +50,13 @@ MUTANTS = {
                       "live = np.arange(Sk)[None, :] < np.arange(Sq)[:, None]"),
     "causal_bottom_right": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                             "live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq)"),
+    "append_causal_strict": ("causal = np.arange(C)[None, :] <= pos[:, None]",
+                             "causal = np.arange(C)[None, :] < pos[:, None]"),
+    "append_pos_off_by_one": ("pos = L + np.arange(T)", "pos = L + 1 + np.arange(T)"),
+    "append_key_unrotated": ("kr = rope(kn[b, hk], pos, rope_base, rope_style) if rope_base > 0 else kn[b, hk]",
+                             "kr = kn[b, hk]"),
+    "append_values_not_written": ("v[b, hk, L:L + T] = vn[b, hk]", "pass"),
+    "append_overflow_inclusive": ("if L < 0 or L + T > C:", "if L < 0 or L + T >= C:"),
     "causal_transposed": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                           "live = np.arange(Sk)[None, :] >= np.arange(Sq)[:, None]"),
 }
