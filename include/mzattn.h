@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MZATTN_VERSION 100 /* major * 10000 + minor * 100 + patch */
+#define MZATTN_VERSION 200 /* major * 10000 + minor * 100 + patch */
 
 /* ---- status codes ------------------------------------------------------ */
 #define MZ_OK 0
@@ -231,6 +231,77 @@ typedef struct mzattn_decode_args {
 int mzattn_decode(const mzattn_decode_args* args, void* stream);
 int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes);
 int mzattn_validate_decode(const mzattn_decode_args* args);
+
+/* ---- mzattn_decode_append ---------------------------------------------- */
+/*
+ * One generation step that appends its own keys and values to the static
+ * cache and takes the filled length from device memory, so the step needs
+ * no host value that changes from step to step and can be recorded once in
+ * a HIP graph and replayed (VoxCPM page, "Memory and speed": each patch
+ * waits on the device for the language models' positions, copied from
+ * Python integers, and under CUDA graphs the attention spans the whole
+ * cache; "What matches upstream", attention bullet: the step attends to a
+ * static cache under an explicit boolean mask, zero and masked past the
+ * current length).
+ *
+ * Row b holds len[b] filled cache rows (device int32, batch stride
+ * len_stride_b, 0 = one length for every row).  Its q_len new tokens take
+ * cache rows and positions len[b] + t, t = 0 .. q_len-1:
+ *   - with rope_base > 0, q and k_new are rotated at that position (pairs
+ *     chosen by rope_style, as in mzattn_fwd_args; every head);
+ *   - the (rotated) k_new and v_new rows are written into k_cache and
+ *     v_cache at that row;
+ *   - query t attends to keys j <= len[b] + t (the filled rows and the new
+ *     tokens up to itself), further restricted to mask[b, h, t, j] != 0
+ *     when mask is not NULL (same layout as mzattn_decode's mask).
+ * Keys past len[b] + q_len are never read.  A row with len[b] < 0 or
+ * len[b] + q_len > cache_len writes nothing into the caches, gets an
+ * all-zero output, and sets *overflow = 1 when overflow is not NULL (the
+ * library never clears it).  The result is the one mzattn_decode gives on
+ * the updated cache with that mask, and it has the same independence of
+ * the key count beyond the last live key.
+ *
+ * Layouts: q and o [batch, heads_q, q_len, head_dim]; k_new, v_new
+ * [batch, heads_kv, q_len, head_dim]; caches [batch, heads_kv, cache_len,
+ * head_dim]; element strides, d contiguous.  dtype: MZ_BF16 or MZ_F16
+ * (MZ_F32: MZ_ERR_UNSUPPORTED).  Other limits as for mzattn_decode.  The
+ * launch depends on cache_len only (one work-group per 128-key chunk of
+ * the whole cache; chunks past len[b] + q_len exit at once).
+ *
+ * workspace: mzattn_decode_append_workspace_size() bytes, 256-byte
+ * aligned, no initialisation; calls sharing one must not overlap in time.
+ */
+typedef struct mzattn_decode_append_args {
+  uint32_t struct_size; /* = sizeof(mzattn_decode_append_args), else MZ_ERR_ABI */
+  int32_t dtype;
+  int32_t batch, heads_q, heads_kv, q_len, head_dim, cache_len;
+  float scale;
+  int32_t rope_style;   /* 0 interleaved, 1 half split */
+  double rope_base;     /* 0: no rotation */
+  const void* q;
+  int64_t q_stride[3];
+  const void* k_new;
+  int64_t k_new_stride[3];
+  const void* v_new;
+  int64_t v_new_stride[3];
+  void* k_cache;        /* rows len[b] .. len[b] + q_len - 1 are written */
+  int64_t k_stride[3];
+  void* v_cache;
+  int64_t v_stride[3];
+  const int32_t* len;   /* device [batch] (or one value, len_stride_b = 0) */
+  int64_t len_stride_b;
+  void* o;
+  int64_t o_stride[3];
+  const uint8_t* mask;  /* optional, [B|1, Hq|1, q_len|1, cache_len] bool */
+  int64_t mask_stride[4];
+  int32_t* overflow;    /* optional device int, set to 1 on overflow */
+  void* workspace;
+  size_t workspace_bytes;
+} mzattn_decode_append_args;
+
+int mzattn_decode_append(const mzattn_decode_append_args* args, void* stream);
+int mzattn_decode_append_workspace_size(const mzattn_decode_append_args* args, size_t* bytes);
+int mzattn_validate_decode_append(const mzattn_decode_append_args* args);
 
 /* ---- misc -------------------------------------------------------------- */
 /* Static description of a status code. */

@@ -3,9 +3,10 @@
 The compute lives in ``libmzattn.so`` (hand-written HIP, C ABI declared in
 ``include/mzattn.h``); this package only marshals torch tensors into it.
 
-    from masked_bidirectional_attention_amd import mzattn_fwd, mzattn_decode
+    from masked_bidirectional_attention_amd import mzattn_fwd, mzattn_decode, mzattn_decode_append
 """
 from ._binding import (  # noqa: F401
+    DecodeAppendCall,
     DecodeCall,
     FwdCall,
     LIB_PATH,
@@ -13,7 +14,8 @@ from ._binding import (  # noqa: F401
     MzattnNotBuilt,
     lib,
     mzattn_decode,
+    mzattn_decode_append,
     mzattn_fwd,
 )
 
-__all__ = ["DecodeCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]
+__all__ = ["DecodeCall", "DecodeAppendCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "mzattn_decode_append", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]

@@ -123,6 +123,41 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodeAppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("cache_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("rope_style", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("q", ctypes.c_void_p),
+        ("q_stride", _i64x3),
+        ("k_new", ctypes.c_void_p),
+        ("k_new_stride", _i64x3),
+        ("v_new", ctypes.c_void_p),
+        ("v_new_stride", _i64x3),
+        ("k_cache", ctypes.c_void_p),
+        ("k_stride", _i64x3),
+        ("v_cache", ctypes.c_void_p),
+        ("v_stride", _i64x3),
+        ("len", ctypes.c_void_p),
+        ("len_stride_b", ctypes.c_int64),
+        ("o", ctypes.c_void_p),
+        ("o_stride", _i64x3),
+        ("mask", ctypes.c_void_p),
+        ("mask_stride", _i64x4),
+        ("overflow", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 # exported C symbols and their signatures
 _SIGNATURES = {
     "mzattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
@@ -135,6 +170,10 @@ _SIGNATURES = {
     "mzattn_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "mzattn_decode_workspace_size": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "mzattn_validate_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs)]),
+    "mzattn_decode_append": (ctypes.c_int, [ctypes.POINTER(DecodeAppendArgs), ctypes.c_void_p]),
+    "mzattn_decode_append_workspace_size": (ctypes.c_int, [ctypes.POINTER(DecodeAppendArgs),
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "mzattn_validate_decode_append": (ctypes.c_int, [ctypes.POINTER(DecodeAppendArgs)]),
     "mzattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mzattn_last_error": (ctypes.c_char_p, []),
     "mzattn_version": (ctypes.c_int, []),
@@ -179,6 +218,12 @@ def new_fwd_args() -> FwdArgs:
 def new_decode_args() -> DecodeArgs:
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
+    return a
+
+
+def new_decode_append_args() -> DecodeAppendArgs:
+    a = DecodeAppendArgs()
+    a.struct_size = ctypes.sizeof(DecodeAppendArgs)
     return a
 
 
@@ -432,3 +477,73 @@ def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
     [B|1, Hq|1, q_len|1, cache_len] or None."""
     return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
                       q_pos=q_pos, rope_style=rope_style, out=out, workspace=workspace, stream=stream)()
+
+
+class DecodeAppendCall:
+    """A marshalled append step (see ``mzattn_decode_append`` in
+    include/mzattn.h): q [B, Hq, q_len, D] and k_new / v_new
+    [B, Hkv, q_len, D], not rotated; the caches [B, Hkv, cache_len, D] get
+    the new rows at len[b] + t; ``length`` is an int32 device tensor [B]
+    (or [1]) holding the filled rows before the step.  Nothing here reads
+    ``length`` on the host, so a call can be captured in a HIP graph and
+    replayed after the caller updates ``length`` on the device.
+    ``overflow`` (optional int32 device tensor [1]) is set to 1 when a row
+    does not fit."""
+
+    def __init__(self, q, k_new, v_new, k_cache, v_cache, length, *, mask=None, scale: float = 0.0,
+                 rope_base: float = 0.0, rope_style: str = "interleaved", overflow=None, out=None,
+                 workspace=None, stream=None):
+        torch = _torch()
+        L = lib()
+        B, Hq, T, D = q.shape
+        Hkv, C = k_cache.shape[1], k_cache.shape[2]
+        a = new_decode_append_args()
+        a.dtype = _dtype_code(q)
+        for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+            if t.dtype != q.dtype:
+                raise MzattnError(MZ_ERR_DTYPE, f"{name} must have q's dtype")
+        a.batch, a.heads_q, a.heads_kv, a.q_len, a.head_dim, a.cache_len = B, Hq, Hkv, T, D, C
+        a.scale = float(scale)
+        a.rope_base = float(rope_base)
+        a.rope_style = _rope_style(rope_style)
+        o = out if out is not None else torch.empty(B, Hq, T, D, dtype=q.dtype, device=q.device)
+        a.q, a.k_new, a.v_new = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr()
+        a.k_cache, a.v_cache, a.o = k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr()
+        a.q_stride, a.k_new_stride, a.v_new_stride = _strides3(q, "q"), _strides3(k_new, "k_new"), _strides3(v_new, "v_new")
+        a.k_stride, a.v_stride, a.o_stride = _strides3(k_cache, "k_cache"), _strides3(v_cache, "v_cache"), _strides3(o, "o")
+        if length.dtype != torch.int32 or length.dim() != 1 or length.shape[0] not in (1, B):
+            raise MzattnError(MZ_ERR_DTYPE, "length must be an int32 tensor [B] or [1]")
+        a.len = length.data_ptr()
+        a.len_stride_b = length.stride(0) if length.shape[0] > 1 else 0
+        keep = [q, k_new, v_new, k_cache, v_cache, length, o]
+        if mask is not None:
+            m, st = _mask_strides(mask, B, Hq, T, C)
+            a.mask, a.mask_stride = m.data_ptr(), st
+            keep.append(m)
+        if overflow is not None:
+            if overflow.dtype != torch.int32 or overflow.numel() < 1:
+                raise MzattnError(MZ_ERR_DTYPE, "overflow must be an int32 tensor")
+            a.overflow = overflow.data_ptr()
+            keep.append(overflow)
+        need = ctypes.c_size_t(0)
+        _check(L.mzattn_decode_append_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        self.stream = torch.cuda.current_stream(q.device) if stream is None else stream
+        if workspace is None:
+            workspace = _WS.get("decode", q.device, self.stream.cuda_stream, need.value, zero=False)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        keep.append(workspace)
+        self.args, self.out, self._keep, self._lib = a, o, keep, L
+
+    def __call__(self):
+        _check(self._lib.mzattn_decode_append(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
+        return self.out
+
+
+def mzattn_decode_append(q, k_new, v_new, k_cache, v_cache, length, *, mask=None, scale: float = 0.0,
+                         rope_base: float = 0.0, rope_style: str = "interleaved", overflow=None, out=None,
+                         workspace=None, stream=None):
+    """One append step (see ``DecodeAppendCall``): writes the new rows into
+    the caches and returns o [B, Hq, q_len, D]."""
+    return DecodeAppendCall(q, k_new, v_new, k_cache, v_cache, length, mask=mask, scale=scale,
+                            rope_base=rope_base, rope_style=rope_style, overflow=overflow, out=out,
+                            workspace=workspace, stream=stream)()

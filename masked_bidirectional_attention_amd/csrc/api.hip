@@ -458,3 +458,113 @@ int mzattn_decode(const mzattn_decode_args* a, void* stream) {
 }
 
 }  // extern "C"
+
+// ---- decode with append ---------------------------------------------------
+namespace {
+
+// The shared checks of mzattn_decode on the equivalent call (whole-cache
+// span, no q_pos rotation), then the append step's own.
+int validate_append_full(const mzattn_decode_append_args* a, mzattn_decode_args* d, DecPlan* pl) {
+  if (a == nullptr) return fail(MZ_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(mzattn_decode_append_args))
+    return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_decode_append_args) %zu", a->struct_size,
+                sizeof(mzattn_decode_append_args));
+  memset(d, 0, sizeof(*d));
+  d->struct_size = sizeof(mzattn_decode_args);
+  d->dtype = a->dtype;
+  d->batch = a->batch; d->heads_q = a->heads_q; d->heads_kv = a->heads_kv; d->q_len = a->q_len;
+  d->head_dim = a->head_dim; d->cache_len = a->cache_len; d->span = a->cache_len;
+  d->scale = a->scale; d->rope_style = a->rope_style; d->rope_base = 0.0;
+  d->q = a->q; d->k_cache = a->k_cache; d->v_cache = a->v_cache; d->o = a->o;
+  for (int i = 0; i < 3; ++i) {
+    d->q_stride[i] = a->q_stride[i]; d->k_stride[i] = a->k_stride[i];
+    d->v_stride[i] = a->v_stride[i]; d->o_stride[i] = a->o_stride[i];
+  }
+  d->mask = a->mask;
+  for (int i = 0; i < 4; ++i) d->mask_stride[i] = a->mask_stride[i];
+  d->workspace = a->workspace; d->workspace_bytes = a->workspace_bytes;
+  if (a->dtype == MZ_F32) return fail(MZ_ERR_UNSUPPORTED, "mzattn_decode_append supports bf16 and fp16");
+  if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
+    return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
+  int st = validate_decode_full(d, pl);
+  if (st != MZ_OK || pl->empty) return st;
+  if (a->cache_len < 1) return fail(MZ_ERR_SHAPE, "cache_len must be >= 1 to append");
+  if (a->k_new == nullptr || a->v_new == nullptr) return fail(MZ_ERR_NULL, "k_new and v_new must not be NULL");
+  if (!aligned(a->k_new, 16) || !aligned(a->v_new, 16)) return fail(MZ_ERR_ALIGN, "k_new / v_new not 16-byte aligned");
+  if ((st = check_strides3(a->k_new_stride, 8, "k_new")) != MZ_OK) return st;
+  if ((st = check_strides3(a->v_new_stride, 8, "v_new")) != MZ_OK) return st;
+  if (a->len == nullptr) return fail(MZ_ERR_NULL, "len must not be NULL");
+  if (a->len_stride_b < 0) return fail(MZ_ERR_STRIDE, "len_stride_b must be >= 0");
+  return MZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mzattn_decode_append_workspace_size(const mzattn_decode_append_args* args, size_t* bytes) {
+  if (bytes == nullptr) return fail(MZ_ERR_NULL, "bytes is NULL");
+  if (args == nullptr) return fail(MZ_ERR_NULL, "args is NULL");
+  if (args->struct_size != sizeof(mzattn_decode_append_args))
+    return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_decode_append_args) %zu", args->struct_size,
+                sizeof(mzattn_decode_append_args));
+  mzattn_decode_args d;
+  memset(&d, 0, sizeof(d));
+  d.struct_size = sizeof(d);
+  d.dtype = args->dtype; d.batch = args->batch; d.heads_q = args->heads_q; d.heads_kv = args->heads_kv;
+  d.q_len = args->q_len; d.head_dim = args->head_dim; d.cache_len = args->cache_len; d.span = args->cache_len;
+  d.scale = args->scale; d.rope_style = args->rope_style;
+  DecPlan pl;
+  const int st = plan_decode(&d, &pl);
+  if (st != MZ_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+int mzattn_validate_decode_append(const mzattn_decode_append_args* args) {
+  mzattn_decode_args d;
+  DecPlan pl;
+  const int st = validate_append_full(args, &d, &pl);
+  return st == MZ_OK ? ok() : st;
+}
+
+int mzattn_decode_append(const mzattn_decode_append_args* a, void* stream) {
+  mzattn_decode_args d;
+  DecPlan pl;
+  const int st = validate_append_full(a, &d, &pl);
+  if (st != MZ_OK) return st;
+  if (pl.empty) return ok();
+  mz::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.dtype = a->dtype;
+  p.B = a->batch; p.Hq = a->heads_q; p.Hkv = a->heads_kv; p.G = a->heads_q / a->heads_kv;
+  p.T = a->q_len; p.R = pl.R; p.C = a->cache_len; p.span = a->cache_len; p.D = a->head_dim;
+  p.n_chunks = pl.n_chunks_max;
+  p.scale_log2 = scale_log2(a->scale, a->head_dim);
+  p.q = a->q;
+  for (int i = 0; i < 3; ++i) p.qs[i] = a->q_stride[i];
+  if (a->rope_base > 0.0) {
+    p.rope = 1;
+    p.rope_style = a->rope_style;
+    p.log2_base = log2(a->rope_base);
+  }
+  p.k = a->k_cache; p.v = a->v_cache; p.o = a->o;
+  p.k_w = a->k_cache; p.v_w = a->v_cache;
+  for (int i = 0; i < 3; ++i) { p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; p.os[i] = a->o_stride[i]; }
+  p.mask = a->mask;
+  if (a->mask)
+    for (int i = 0; i < 4; ++i) p.ms[i] = a->mask_stride[i];
+  p.app = 1;
+  p.len = a->len; p.len_sb = a->len_stride_b;
+  p.k_new = a->k_new; p.v_new = a->v_new;
+  for (int i = 0; i < 3; ++i) { p.kn_s[i] = a->k_new_stride[i]; p.vn_s[i] = a->v_new_stride[i]; }
+  p.overflow = a->overflow;
+  char* ws = static_cast<char*>(a->workspace);
+  p.part_ml = reinterpret_cast<float2*>(ws + pl.off_ml);
+  p.part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
+  const hipError_t e = mz::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MZ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -69,8 +69,8 @@ __global__ void decode_q_rotate32_kernel(const DecodeParams p) {
   dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
 }
 
-__device__ inline bool dec_live(const DecodeParams& p, int b, int kvh, int n, int key) {
-  if (n >= p.R || key >= p.span) return false;
+__device__ inline bool dec_live(const DecodeParams& p, int b, int kvh, int n, int key, int span) {
+  if (n >= p.R || key >= span) return false;
   if (p.mask == nullptr) return true;
   const int g = n / p.T, t = n % p.T;
   const int h = kvh * p.G + g;
@@ -201,7 +201,58 @@ __global__ __launch_bounds__(256) void decode_merge32_kernel(const DecodeParams 
 // [chunk*128 + 32w, +32); rows n = g*q_len + t in NB blocks of 16.
 // S^T = K Q^T, then O^T = V^T P^T with V^T read transposed from LDS.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NB>
+// Rotate the 8 * NS elements a lane holds of one row (d = s*32 + g4*8 + e)
+// with the row's cosines and sines cs[i] (pair i): pairs (2i, 2i+1) inside
+// each 8-element piece, or with half-split pairing element d of piece s
+// with element d + D/2, which is the same element of piece s + NS/2 in the
+// same lane.
+template <typename T, int NS>
+__device__ inline void rope_lane_row(uint4 (&x)[NS], const float2* cs, int g4, int style) {
+  if (style == 1) {
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+      uint32_t lo[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+      uint32_t hi[4] = {x[s + NS / 2].x, x[s + NS / 2].y, x[s + NS / 2].z, x[s + NS / 2].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float r[2][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
+          const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
+          const float2 w = cs[s * 32 + g4 * 8 + 2 * t + e];
+          r[0][e] = fmaf(a, w.x, -c * w.y);
+          r[1][e] = fmaf(c, w.x, a * w.y);
+        }
+        lo[t] = Elem<T>::pack2(r[0][0], r[0][1]);
+        hi[t] = Elem<T>::pack2(r[1][0], r[1][1]);
+      }
+      x[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      x[s + NS / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      uint32_t w[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float a = Elem<T>::to_f32((uint16_t)(w[t] & 0xFFFF));
+        const float c = Elem<T>::to_f32((uint16_t)(w[t] >> 16));
+        const float2 r = cs[(s * 32 + g4 * 8) / 2 + t];
+        w[t] = Elem<T>::pack2(fmaf(a, r.x, -c * r.y), fmaf(c, r.x, a * r.y));
+      }
+      x[s] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// APP: the append step (mzattn_decode_append).  The row's filled length
+// len[b] is read here; keys from len[b] + q_len on are past the span, the
+// new rows [len[b], len[b] + q_len) are loaded from k_new / v_new, rotated
+// at their position and written into the caches by the one wave that owns
+// them, q is rotated at len[b] + t in registers, and query t sees keys
+// j <= len[b] + t only.
+template <typename T, int D, int NB, bool APP>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int AS = D + 4;        // LDS row stride of the parked acc blocks (floats)
   constexpr int NS = D / 32;       // k-steps of K Q^T
@@ -215,6 +266,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   __shared__ float red_m[4][RP];
   __shared__ float red_l[4][RP];
   __shared__ uint8_t live_s[RP][DEC_CHUNK];
+  // (append) cosines and sines of the new tokens' positions len + t
+  __shared__ float2 cs_s[APP ? 16 : 1][APP ? D / 2 : 1];
   static_assert(sizeof(float) * RP * AS <= sizeof(uint16_t) * 4 * 32 * VSD, "acc fold reuses the V region");
   float* acc_lds = reinterpret_cast<float*>(&Vs[0][0]);
 
@@ -229,24 +282,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const uint16_t* kbase = (const uint16_t*)p.k + b * p.ks[0] + kvh * p.ks[1];
   const uint16_t* vbase = (const uint16_t*)p.v + b * p.vs[0] + kvh * p.vs[1];
 
+  // keys [0, span_b) of this row are considered
+  int lenb = 0, span_b = p.span;
+  if constexpr (APP) {
+    lenb = p.len[(int64_t)b * p.len_sb];
+    const bool fits = lenb >= 0 && (int64_t)lenb + p.T <= (int64_t)p.C;
+    span_b = fits ? lenb + p.T : 0;
+    if (!fits && c == 0 && kvh == 0 && tid == 0 && p.overflow != nullptr) *p.overflow = 1;
+  }
+  // (append) this chunk holds some of the new rows: never skipped, so they
+  // are written into the caches whatever the mask says
+  const bool holds_new = APP && c * DEC_CHUNK < span_b && (c + 1) * DEC_CHUNK > lenb;
+
   // ---- a chunk in which no (row, key) pair is live is the identity of the
   // merge: found from the mask alone, its K/V are never read.  The scan
   // keeps the chunk's liveness bytes in LDS (one row when the mask is
   // broadcast over heads and queries) for the score test below, so no mask
   // load sits among the K/V loads.
   const bool bcast = p.mask != nullptr && p.ms[1] == 0 && p.ms[2] == 0;
-  // (an empty span has one chunk and no key index valid to load)
-  bool dead = p.span <= 0;
+  // (a chunk at or past the span, e.g. the one chunk of an empty span, has
+  // no key index valid to load)
+  bool dead = span_b <= c * DEC_CHUNK;
   if (p.mask != nullptr && !dead) {
     const int ckey0 = c * DEC_CHUNK;
     const int rows = bcast ? 1 : p.R;
     bool any = false;
     for (int idx = tid; idx < rows * DEC_CHUNK; idx += 256) {
-      const bool lv = dec_live(p, b, kvh, idx / DEC_CHUNK, ckey0 + idx % DEC_CHUNK);
+      const bool lv = dec_live(p, b, kvh, idx / DEC_CHUNK, ckey0 + idx % DEC_CHUNK, span_b);
       live_s[idx / DEC_CHUNK][idx % DEC_CHUNK] = lv;
       any |= lv;
     }
-    dead = !__syncthreads_or(any);
+    dead = !__syncthreads_or(any) && !holds_new;
   }
   if (dead) {
     const int64_t pb = ((int64_t)unit * p.n_chunks + c) * p.R;
@@ -261,20 +327,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   // (in bounds; their scores are masked to -inf below, so their weights
   // are exact zeros).  Conditional loads would each end in a wait, making
   // the loads one dependent round trip after another.
-  const int klast = p.span - 1;
-  u32x4_t vr[NVL];  // a native vector type: one load each, kept in registers
-#pragma unroll
-  for (int it = 0; it < NVL; ++it) {
-    const int r = it * RPI + lane / CH, cc = lane % CH;
-    const int key = min(key0 + r, klast);
-    vr[it] = *(const u32x4_t*)(vbase + (int64_t)key * p.vs[2] + cc * 8);
-  }
-  uint4 kf[2][NS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = min(key0 + kb * 16 + l16, klast);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) kf[kb][s] = *(const uint4*)(kbase + (int64_t)key * p.ks[2] + s * 32 + g4 * 8);
+  const int klast = span_b - 1;
+  const uint16_t* knew = nullptr;
+  const uint16_t* vnew = nullptr;
+  if constexpr (APP) {
+    knew = (const uint16_t*)p.k_new + b * p.kn_s[0] + kvh * p.kn_s[1];
+    vnew = (const uint16_t*)p.v_new + b * p.vn_s[0] + kvh * p.vn_s[1];
   }
   uint4 qf[NB][NS];
 #pragma unroll
@@ -287,9 +345,59 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
       qf[nb][s] = *(const uint4*)((const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t * p.qs[2] + s * 32 +
                                   g4 * 8);
   }
+  u32x4_t vr[NVL];  // a native vector type: one load each, kept in registers
+#pragma unroll
+  for (int it = 0; it < NVL; ++it) {
+    const int r = it * RPI + lane / CH, cc = lane % CH;
+    const int key = min(key0 + r, klast);
+    const uint16_t* row = (APP && key >= lenb) ? vnew + (int64_t)(key - lenb) * p.vn_s[2] : vbase + (int64_t)key * p.vs[2];
+    vr[it] = *(const u32x4_t*)(row + cc * 8);
+  }
+  uint4 kf[2][NS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = min(key0 + kb * 16 + l16, klast);
+    const uint16_t* row = (APP && key >= lenb) ? knew + (int64_t)(key - lenb) * p.kn_s[2] : kbase + (int64_t)key * p.ks[2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[kb][s] = *(const uint4*)(row + s * 32 + g4 * 8);
+  }
   // every load above is issued before the first use of any of them (the
   // scheduler would otherwise start the V loads after the K.Q MFMAs)
   asm volatile("" ::: "memory");
+  if constexpr (APP) {
+    // q at len + t (its loads came first: this overlaps the K/V loads)
+    if (p.rope) {
+      for (int idx = tid; idx < p.T * (D / 2); idx += 256)
+        cs_s[idx / (D / 2)][idx % (D / 2)] = rope_cs_direct(lenb + idx / (D / 2), idx % (D / 2), D, p.log2_base);
+      __syncthreads();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = min(nb * 16 + l16, p.R - 1);
+        rope_lane_row<T, NS>(qf[nb], cs_s[n % p.T], g4, p.rope_style);
+      }
+    }
+    // the new rows this wave holds: K rotated at its position, then both
+    // written into the caches (every lane of the row writes its pieces)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = key0 + kb * 16 + l16;
+      if (key >= lenb && key < span_b) {
+        if (p.rope) rope_lane_row<T, NS>(kf[kb], cs_s[key - lenb], g4, p.rope_style);
+        uint16_t* dst = (uint16_t*)p.k_w + b * p.ks[0] + kvh * p.ks[1] + (int64_t)key * p.ks[2];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) *(uint4*)(dst + s * 32 + g4 * 8) = kf[kb][s];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NVL; ++it) {
+      const int r = it * RPI + lane / CH, cc = lane % CH;
+      const int key = key0 + r;
+      if (key >= lenb && key < span_b) {
+        uint16_t* dst = (uint16_t*)p.v_w + b * p.vs[0] + kvh * p.vs[1] + (int64_t)key * p.vs[2];
+        *(u32x4_t*)(dst + cc * 8) = vr[it];
+      }
+    }
+  }
   // liveness of this lane's score elements (mask bytes from the scan)
   bool live[2][NB][4];
 #pragma unroll
@@ -299,7 +407,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int n = nb * 16 + l16, j = wave * 32 + kb * 16 + g4 * 4 + v;
-        const bool in = n < p.R && c * DEC_CHUNK + j < p.span;
+        const int key = c * DEC_CHUNK + j;
+        const bool in = n < p.R && key < span_b && (!APP || key <= lenb + n % p.T);
         live[kb][nb][v] = in && (p.mask == nullptr || live_s[bcast ? 0 : n][j] != 0);
       }
   // V rows into this wave's LDS region
@@ -452,7 +561,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeParams p) {
     const int n = idx / DEC_CHUNK, j = idx % DEC_CHUNK;
     const int key = key0 + j;
     float x = -INFINITY;
-    if (dec_live(p, b, kvh, n, key)) {
+    if (dec_live(p, b, kvh, n, key, p.span)) {
       const int g = n / p.T, t = n % p.T;
       const int h = kvh * p.G + g;
       const float* qrow = (const float*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t * p.qs[2];
@@ -495,15 +604,20 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+template <typename T, int D, bool APP>
+static void launch_dec16_k(const DecodeParams& p, unsigned nblk, hipStream_t s) {
+  if (p.R <= 16) decode_mfma_kernel<T, D, 1, APP><<<dim3(nblk), dim3(256), 0, s>>>(p);
+  else if (p.R <= 32) decode_mfma_kernel<T, D, 2, APP><<<dim3(nblk), dim3(256), 0, s>>>(p);
+  else decode_mfma_kernel<T, D, 4, APP><<<dim3(nblk), dim3(256), 0, s>>>(p);
+}
 template <typename T, int D>
 static void launch_dec16(const DecodeParams& p, unsigned nblk, hipStream_t s) {
-  if (p.R <= 16) decode_mfma_kernel<T, D, 1><<<dim3(nblk), dim3(256), 0, s>>>(p);
-  else if (p.R <= 32) decode_mfma_kernel<T, D, 2><<<dim3(nblk), dim3(256), 0, s>>>(p);
-  else decode_mfma_kernel<T, D, 4><<<dim3(nblk), dim3(256), 0, s>>>(p);
+  if (p.app) launch_dec16_k<T, D, true>(p, nblk, s);
+  else launch_dec16_k<T, D, false>(p, nblk, s);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  if (p.rope) {
+  if (p.rope && !p.app) {  // (the append step rotates q in the chunk kernel)
     const int64_t n = (int64_t)p.B * p.Hq * p.T * (p.D / 2);
     const unsigned nb = (unsigned)((n + 255) / 256);
     if (p.dtype == 0) decode_q_rotate32_kernel<<<dim3(nb), dim3(256), 0, s>>>(p);

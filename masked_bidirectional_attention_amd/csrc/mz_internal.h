@@ -83,6 +83,19 @@ struct DecodeParams {
   double log2_base;
   int rope;
   int rope_style;  // 0 interleaved, 1 half split
+  // append step (mzattn_decode_append): the new tokens' rows come from
+  // k_new / v_new, go into the caches at len[b] + t, and rotate in the
+  // chunk kernel
+  int app;
+  const int32_t* len;
+  int64_t len_sb;
+  const void* k_new;
+  int64_t kn_s[3];
+  const void* v_new;
+  int64_t vn_s[3];
+  void* k_w;  // the caches, writable (same as k / v)
+  void* v_w;
+  int32_t* overflow;
   // workspace
   float2* part_ml;     // [B][Hkv][n_chunks][R]   (m in log2 units, l)
   float* part_acc;     // [B][Hkv][n_chunks][R][D]

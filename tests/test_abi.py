@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.mzattn_version() == 100
+    assert lib.mzattn_version() == 200
     for code in range(0, -11, -1):
         msg = lib.mzattn_strerror(code).decode()
         assert msg and msg != "unknown status", code
@@ -60,7 +60,8 @@ def _c_layout(struct, fields):
     return [int(x) for x in out]
 
 
-@pytest.mark.parametrize("cls,cname", [(B.FwdArgs, "mzattn_fwd_args"), (B.DecodeArgs, "mzattn_decode_args")])
+@pytest.mark.parametrize("cls,cname", [(B.FwdArgs, "mzattn_fwd_args"), (B.DecodeArgs, "mzattn_decode_args"),
+                                      (B.DecodeAppendArgs, "mzattn_decode_append_args")])
 def test_struct_layout_matches_header(cls, cname):
     fields = [f for f, _ in cls._fields_]
     got = _c_layout(cname, fields)
@@ -337,3 +338,74 @@ def test_compute_without_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libmzattn.so")
     with pytest.raises(B.MzattnNotBuilt):
         B.lib()
+
+
+# --------------------------------------------------------------------------
+# mzattn_decode_append (host checks only)
+# --------------------------------------------------------------------------
+
+def good_app(B_=2, Hq=16, Hkv=2, T=1, C=8192, D=128):
+    a = B.new_decode_append_args()
+    a.dtype = B.MZ_BF16
+    a.batch, a.heads_q, a.heads_kv, a.q_len, a.head_dim, a.cache_len = B_, Hq, Hkv, T, D, C
+    a.q, a.k_new, a.v_new = FAKE, FAKE + 0x100000, FAKE + 0x200000
+    a.k_cache, a.v_cache, a.o = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+    a.q_stride = a.o_stride = B._i64x3(Hq * T * D, T * D, D)
+    a.k_new_stride = a.v_new_stride = B._i64x3(Hkv * T * D, T * D, D)
+    a.k_stride = a.v_stride = B._i64x3(Hkv * C * D, C * D, D)
+    a.len, a.len_stride_b = FAKE + 0x4000000, 1
+    a.rope_base = 1e4
+    return a
+
+
+def vapp(L, a):
+    need = ctypes.c_size_t(0)
+    st = L.mzattn_decode_append_workspace_size(ctypes.byref(a), ctypes.byref(need))
+    if st == 0:
+        a.workspace, a.workspace_bytes = FAKE + 0x8000000, need.value
+    return L.mzattn_validate_decode_append(ctypes.byref(a))
+
+
+def test_decode_append_valid(lib):
+    assert vapp(lib, good_app()) == 0
+    a = good_app(T=4, Hq=32, Hkv=2)
+    a.mask, a.mask_stride = FAKE, B._i64x4(8192, 0, 0, 1)
+    a.overflow = FAKE + 0x5000000
+    a.len_stride_b = 0
+    assert vapp(lib, a) == 0
+
+
+def test_decode_append_workspace_matches_decode(lib):
+    """The append step needs the decode step's workspace for the whole
+    cache (no rotated-q copy: q rotates in the chunk kernel)."""
+    a = good_app()
+    need = ctypes.c_size_t(0)
+    assert lib.mzattn_decode_append_workspace_size(ctypes.byref(a), ctypes.byref(need)) == 0
+    d, nd = good_dec(span=8192)
+    assert lib.mzattn_decode_workspace_size(ctypes.byref(d), ctypes.byref(nd)) == 0
+    assert need.value == nd.value
+
+
+def app_cases():
+    def m(field, value):
+        return lambda a: setattr(a, field, value)
+    return [
+        ("struct_size", m("struct_size", 4), B.MZ_ERR_ABI),
+        ("fp32", m("dtype", B.MZ_F32), B.MZ_ERR_UNSUPPORTED),
+        ("len_null", m("len", None), B.MZ_ERR_NULL),
+        ("len_stride_neg", m("len_stride_b", -1), B.MZ_ERR_STRIDE),
+        ("k_new_null", m("k_new", None), B.MZ_ERR_NULL),
+        ("v_new_misaligned", m("v_new", FAKE + 0x200000 + 2), B.MZ_ERR_ALIGN),
+        ("k_new_stride", m("k_new_stride", B._i64x3(2 * 128, 128, 129)), B.MZ_ERR_ALIGN),
+        ("rope_base_one", m("rope_base", 1.0), B.MZ_ERR_VALUE),
+        ("cache_empty", m("cache_len", 0), B.MZ_ERR_SHAPE),
+        ("q_len17", m("q_len", 17), B.MZ_ERR_SHAPE),
+        ("gqa_ratio", m("heads_kv", 3), B.MZ_ERR_SHAPE),
+    ]
+
+
+@pytest.mark.parametrize("name,edit,code", app_cases(), ids=[c[0] for c in app_cases()])
+def test_decode_append_rejects(lib, name, edit, code):
+    a = good_app()
+    edit(a)
+    assert vapp(lib, a) == code, (name, lib.mzattn_last_error())

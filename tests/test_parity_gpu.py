@@ -11,7 +11,7 @@ import torch
 
 from masked_bidirectional_attention_amd import workloads as W
 from oracle import mzref
-from tests.gpu_helpers import (assert_parity, bits, dev, oracle_decode, oracle_fwd, run_decode,
+from tests.gpu_helpers import (DEV, assert_parity, bits, dev, oracle_decode, oracle_fwd, run_decode,
                                run_fwd, to64)
 
 pytestmark = pytest.mark.gpu
@@ -445,3 +445,117 @@ def test_decode_repeated_calls_share_workspace(dtype):
             o = call()
             torch.cuda.synchronize()
             assert_parity(dtype, o, oracle_decode(c), f"{c.name} span={c.span} pass {rep}")
+
+
+# --------------------------------------------------------------------------
+# decode with append: the filled length is read on the device
+# --------------------------------------------------------------------------
+
+def _append_case(seed, B, Hq, Hkv, T, C, D, dtype, lens, mask_kind="none"):
+    gen = torch.Generator().manual_seed(seed)
+    cast = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    q = torch.randn(B, Hq, T, D, generator=gen).to(cast)
+    kn = torch.randn(B, Hkv, T, D, generator=gen).to(cast)
+    vn = torch.randn(B, Hkv, T, D, generator=gen).to(cast)
+    kc = torch.randn(B, Hkv, C, D, generator=gen).to(cast)
+    vc = torch.randn(B, Hkv, C, D, generator=gen).to(cast)
+    rng = np.random.default_rng(seed + 7)
+    mask = None
+    if mask_kind == "bcast":
+        mask = torch.from_numpy(rng.random((B, 1, 1, C)) < 0.9)
+    elif mask_kind == "heads":
+        mask = torch.from_numpy(rng.random((B, Hq, T, C)) < 0.8)
+    return q, kn, vn, kc, vc, torch.tensor(lens, dtype=torch.int32), mask
+
+
+@pytest.mark.parametrize("cfg", [
+    # B, Hq, Hkv, T, C, D, dtype, lens, rope_style, mask
+    (2, 16, 2, 1, 8192, 128, "bf16", [8191, 300], "interleaved", "none"),
+    (2, 16, 2, 1, 8192, 128, "f16", [0, 4000], "half", "bcast"),
+    (1, 32, 2, 4, 1200, 128, "bf16", [777], "interleaved", "heads"),
+    (2, 8, 1, 2, 700, 64, "bf16", [127, 255], "half", "none"),
+    (3, 4, 4, 3, 300, 64, "f16", [0, 10, 298], "interleaved", "bcast"),   # row 2 overflows
+], ids=lambda c: "x".join(map(str, c[:6])) + f"-{c[6]}-{c[8]}-{c[9]}")
+def test_decode_append(cfg):
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, T, C, D, dtype, lens, style, mk = cfg
+    q, kn, vn, kc, vc, ln, mask = _append_case(zlib.crc32(repr(cfg).encode()) % 10000, B, Hq, Hkv, T, C, D, dtype,
+                                               lens, mk)
+    kc_d, vc_d = dev(kc), dev(vc)
+    ovf = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print(f"[append] {cfg}", flush=True)
+    o = mz.mzattn_decode_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, dev(ln), mask=dev(mask), rope_base=1e4,
+                                rope_style=style, overflow=ovf)
+    torch.cuda.synchronize()
+    ref, k_rows, overflow = mzref.mzref_decode_append(
+        dtype, W.to_bits(q), W.to_bits(kn), W.to_bits(vn), W.to_bits(kc), W.to_bits(vc), lens,
+        mask=None if mask is None else mask.numpy(), rope_base=1e4, rope_style=style)
+    assert_parity(dtype, o, ref, f"append {cfg}")
+    assert int(ovf.item()) == int(overflow.any())
+    kc2, vc2 = kc_d.cpu(), vc_d.cpu()
+    for b in range(B):
+        L = lens[b]
+        if overflow[b]:
+            assert torch.all(o[b] == 0)
+            assert torch.equal(kc2[b], kc[b]) and torch.equal(vc2[b], vc[b]), "overflow row touched the cache"
+            continue
+        # untouched rows stay bit-identical; the new V rows are copied bit
+        # for bit; the new K rows are the rotated keys in the storage type
+        assert torch.equal(kc2[b, :, :L], kc[b, :, :L]) and torch.equal(kc2[b, :, L + T:], kc[b, :, L + T:])
+        assert torch.equal(vc2[b, :, :L], vc[b, :, :L]) and torch.equal(vc2[b, :, L + T:], vc[b, :, L + T:])
+        assert torch.equal(vc2[b, :, L:L + T], vn[b])
+        got = kc2[b, :, L:L + T].double().numpy()
+        ulp = 2.0 ** (-7 if dtype == "bf16" else -10)
+        assert np.all(np.abs(got - k_rows[b]) <= ulp * np.abs(k_rows[b]) + 1e-6), "appended key rows"
+
+
+def test_decode_append_equals_decode_on_updated_cache():
+    """The append step gives the bits mzattn_decode gives on the updated
+    cache with the mask j <= len + t and q rotated at len + t."""
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, T, C, D = 2, 16, 2, 3, 2048, 128
+    lens = [1000, 2040]
+    q, kn, vn, kc, vc, ln, _ = _append_case(91, B, Hq, Hkv, T, C, D, "bf16", lens)
+    kc_d, vc_d = dev(kc), dev(vc)
+    o1 = mz.mzattn_decode_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, dev(ln), rope_base=1e6)
+    m = torch.zeros(B, 1, T, C, dtype=torch.bool)
+    pos = torch.zeros(B, T, dtype=torch.int32)
+    for b in range(B):
+        for t in range(T):
+            m[b, 0, t, :lens[b] + t + 1] = True
+            pos[b, t] = lens[b] + t
+    o2 = mz.mzattn_decode(dev(q), kc_d, vc_d, span=C, mask=dev(m), rope_base=1e6, q_pos=dev(pos))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2))
+
+
+def test_decode_append_graph_replay():
+    """Recorded once in a HIP graph, replayed while the length advances on
+    the device between replays: every replay equals an eager call on the
+    same cache state."""
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, T, C, D = 2, 16, 2, 1, 4096, 128
+    q, kn, vn, kc, vc, _, _ = _append_case(92, B, Hq, Hkv, T, C, D, "bf16", [0, 0])
+    s = torch.cuda.Stream()
+    length = torch.tensor([100, 2500], dtype=torch.int32, device=DEV)
+    kc_g, vc_g = dev(kc), dev(vc)
+    dq, dkn, dvn = dev(q), dev(kn), dev(vn)
+    call = mz.DecodeAppendCall(dq, dkn, dvn, kc_g, vc_g, length, rope_base=1e4, stream=s)
+    kc_e, vc_e = kc_g.clone(), vc_g.clone()     # the eager twin's caches
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    # capture recorded the work without running it: the caches are unchanged
+    assert torch.equal(kc_g, kc_e)
+    for step in range(4):
+        lens_now = length.clone()
+        g.replay()
+        torch.cuda.synchronize()
+        o_graph = call.out.clone()
+        o_eager = mz.mzattn_decode_append(dq, dkn, dvn, kc_e, vc_e, lens_now, rope_base=1e4)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o_graph), bits(o_eager)), f"replay {step}"
+        assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"caches after replay {step}"
+        length += 1                                  # next position, on the device
