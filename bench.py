@@ -68,6 +68,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def append_bytes(L):
+    """The append step at fill L: K and V rows of the L cached keys and of
+    the new one read (B 2 x Hkv 2 x (L + 1) x D 128 x 2 bytes x 2), the new
+    K/V rows written, q and o (2 x 16 x 128 x 2 each); no mask."""
+    return 2 * 2 * (L + 1) * 128 * 2 * 2 + 2 * 2 * 128 * 2 * 2 + 2 * (2 * 16 * 128 * 2)
+
+
 COPY_BYTES = 64 * 1024 * 1024
 
 
@@ -314,6 +321,56 @@ def main(argv=None):
               "TFLOP/s": round(cp_gflop / cp_us * 1e3, 1),
               "frac": round(cp_gflop / cp_us * 1e3 / PEAK_BF16_TFLOPS, 4)}
 
+    # ---- the append step (reported, not the headline): the static-cache
+    # step that reads the filled length on the device, rotates q and the new
+    # key, writes the new K/V rows into the cache and attends keys
+    # j <= len; eagerly and as a replayed HIP graph.  The cache copies rotate
+    # as above; the length stays fixed so every call writes the same rows.
+    gen = torch.Generator().manual_seed(4)
+    aq = torch.randn(2, 16, 1, 128, generator=gen).to(torch.bfloat16).to(dev)
+    akn = torch.randn(2, 2, 1, 128, generator=gen).to(torch.bfloat16).to(dev)
+    avn = torch.randn(2, 2, 1, 128, generator=gen).to(torch.bfloat16).to(dev)
+    append = []
+    for L in (256, 1023, 3099, 8191):
+        length = torch.full((2,), L, dtype=torch.int32, device=dev)
+        calls = [mz.DecodeAppendCall(aq, akn, avn, kc, vc, length, rope_base=1e4, scale=c4.scale)
+                 for kc, vc in copies[:8]]
+        for i in range(16):
+            calls[i % 8]()
+        torch.cuda.synchronize()
+        n = 48
+        tot = 0.0
+        for i in range(n):
+            e0.record()
+            calls[i % 8]()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        eager_us = tot / n * 1e3
+        # the same step as a graph: 8 steps (one per cache copy) per replay
+        gs = torch.cuda.Stream()
+        gcalls = [mz.DecodeAppendCall(aq, akn, avn, kc, vc, length, rope_base=1e4, scale=c4.scale, stream=gs)
+                  for kc, vc in copies[:8]]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for c_ in gcalls:
+                c_()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(6):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) / (6 * 8) * 1e3
+        nbytes = append_bytes(L)
+        append.append({"filled": L, "eager_us": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+                       "GB/s_graph": round(nbytes / (graph_us * 1e-6) / 1e9, 1),
+                       "algorithmic_mb": round(nbytes / 1e6, 3)})
+        del g
+
     traffic = {}
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
@@ -376,6 +433,9 @@ def main(argv=None):
             "by_fill": by_fill,
         },
         "causal_prefill": causal,
+        "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
+                                      "length on the device, RoPE base 1e4 on q and the new key",
+                          "by_fill": append},
         "device": props.name,
     }
     if not a.no_cpu_baseline:
