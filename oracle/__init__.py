@@ -12,6 +12,8 @@ from .mzref import (  # noqa: F401
     live_set_fwd,
     mzref_decode,
     mzref_decode_append,
+    rope_cos_sin,
+    round_bf16,
     mzref_fwd,
     parity_stats,
     rope_interleaved,

@@ -110,12 +110,61 @@ def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
     return np.power(float(base), -2.0 * i / head_dim)
 
 
-def rope_interleaved(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to fp32 and then to bf16 (round to nearest even on
+    the upper 16 bits of the fp32 pattern), returned as fp64."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def rope_cos_sin(pos, head_dim: int, base: float, precision: str = "exact", factors=None, mscale: float = 1.0):
+    """cos and sin of the rotation angles, [..., S, D/2] for pos [..., S].
+
+    theta_i = base^(-2i/D) / factors[i] (LongRoPE's per-dimension factors,
+    the MiniCPM-4 LM of the VoxCPM page, 'How it works'; factors None = 1);
+    mscale multiplies cos and sin (LongRoPE's attention factor).
+    precision 'exact': the angle pos * theta_i and its cos / sin in fp64.
+    'fp16' (F5-TTS page, 'What matches upstream': on GPU inv_freq and the
+    angles are fp16): theta_i and pos rounded to fp16, their product rounded
+    to fp16, cos / sin of it rounded to fp16, then times mscale.
+    'bf16_table' (VoxCPM page, 'What matches upstream': the LongRoPE table
+    is built in fp32 and rounded with the model to bf16): the fp32 product
+    of fp32 pos and fp32 theta_i, cos / sin rounded to fp32, times mscale
+    in fp32, rounded to bf16."""
+    theta = rope_inv_freq(head_dim, base)
+    if factors is not None:
+        theta = theta / np.asarray(factors, dtype=np.float64)
+    p = np.asarray(pos, dtype=np.float64)[..., None]
+    if precision == "exact":
+        ang = p * theta
+        return np.cos(ang) * mscale, np.sin(ang) * mscale
+    if precision == "fp16":
+        th16 = theta.astype(np.float16).astype(np.float64)
+        p16 = p.astype(np.float16).astype(np.float64)
+        a16 = (p16 * th16).astype(np.float16).astype(np.float64)
+        c = np.cos(a16).astype(np.float16).astype(np.float64)
+        s_ = np.sin(a16).astype(np.float16).astype(np.float64)
+        return c * mscale, s_ * mscale
+    if precision == "bf16_table":
+        a32 = p.astype(np.float32) * theta.astype(np.float32)
+        m32 = np.float32(mscale)
+        c = np.cos(a32.astype(np.float64)).astype(np.float32) * m32
+        s_ = np.sin(a32.astype(np.float64)).astype(np.float32) * m32
+        return round_bf16(c), round_bf16(s_)
+    raise ValueError(precision)
+
+
+def rope_interleaved(x: np.ndarray, pos: np.ndarray, base: float, precision: str = "exact", factors=None,
+                     mscale: float = 1.0) -> np.ndarray:
     """Rotate adjacent pairs (x_2i, x_2i+1) of every row of x [..., S, D]
     by the angle pos * theta_i, pos [S] (or broadcastable to x[..., 0])."""
     D = x.shape[-1]
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, base)
-    c, s = np.cos(ang), np.sin(ang)
+    if precision == "exact" and factors is None and mscale == 1.0:
+        ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, base)
+        c, s = np.cos(ang), np.sin(ang)
+    else:
+        c, s = rope_cos_sin(pos, D, base, precision, factors, mscale)
     x0, x1 = x[..., 0::2], x[..., 1::2]
     out = np.empty_like(x)
     out[..., 0::2] = x0 * c - x1 * s
@@ -123,14 +172,14 @@ def rope_interleaved(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return out
 
 
-def rope_half_split(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+def rope_half_split(x: np.ndarray, pos: np.ndarray, base: float, precision: str = "exact", factors=None,
+                    mscale: float = 1.0) -> np.ndarray:
     """Rotate the pairs (x_i, x_i+D/2) of every row of x [..., S, D] by the
     angle pos * theta_i: the "rotate half" pairing of GPT-NeoX / Llama-style
     models, offered beside the interleaved one (the pages' other models; the
     survey's RoPE-variants item).  Same frequencies and rotation sense."""
     D = x.shape[-1]
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, base)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = rope_cos_sin(pos, D, base, precision, factors, mscale)
     x0, x1 = x[..., :D // 2], x[..., D // 2:]
     out = np.empty_like(x)
     out[..., :D // 2] = x0 * c - x1 * s
@@ -138,12 +187,14 @@ def rope_half_split(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return out
 
 
-def rope(x: np.ndarray, pos: np.ndarray, base: float, style: str = "interleaved") -> np.ndarray:
-    """The rotation of one pairing: 'interleaved' (default) or 'half'."""
+def rope(x: np.ndarray, pos: np.ndarray, base: float, style: str = "interleaved", precision: str = "exact",
+         factors=None, mscale: float = 1.0) -> np.ndarray:
+    """The rotation of one pairing: 'interleaved' (default) or 'half', with
+    the cos / sin of rope_cos_sin."""
     if style == "interleaved":
-        return rope_interleaved(x, pos, base)
+        return rope_interleaved(x, pos, base, precision, factors, mscale)
     if style == "half":
-        return rope_half_split(x, pos, base)
+        return rope_half_split(x, pos, base, precision, factors, mscale)
     raise ValueError(style)
 
 
@@ -229,7 +280,8 @@ def live_set_fwd(B, Hq, Sq, Sk, mask_kind, mask=None, seg_q=None, seg_k=None):
 def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
               rope_base: float = 0.0, pe_attn_head: int = -1,
               pos_q=None, pos_k=None, mask_kind: str = "none", mask=None,
-              seg_q=None, seg_k=None, heads=None, rope_style: str = "interleaved"):
+              seg_q=None, seg_k=None, heads=None, rope_style: str = "interleaved",
+              rope_precision: str = "exact", rope_factors=None, rope_mscale: float = 1.0):
     """Oracle of the bidirectional forward.
 
     q_bits [B, Hq, Sq, D], k_bits / v_bits [B, Hkv, Sk, D] (storage bits
@@ -278,15 +330,16 @@ def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
             hk = h // G
             qh, kh, vh = q[b, h], k[b, hk], v[b, hk]
             if h < n_rot:
-                qh = rope(qh, pq[b], rope_base, rope_style)
-                kh = rope(kh, pk[b], rope_base, rope_style)
+                qh = rope(qh, pq[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)
+                kh = rope(kh, pk[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)
             lv = live[b, h if live.shape[1] > 1 else 0]
             o[b, h], lse[b, h] = attend(qh, kh, vh, lv, scale)
     return o, lse
 
 
 def mzref_decode(dtype: str, q_bits, k_bits, v_bits, *, span: int, mask=None,
-                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved"):
+                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
+                 rope_precision: str = "exact", rope_factors=None, rope_mscale: float = 1.0):
     """Oracle of one static-cache step (VoxCPM page, 'What matches
     upstream', attention bullet, and 'Memory and speed', attention_span).
 
@@ -315,13 +368,14 @@ def mzref_decode(dtype: str, q_bits, k_bits, v_bits, *, span: int, mask=None,
         for h in range(Hq):
             qh = q[b, h]
             if rope_base > 0:
-                qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style)
+                qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)
             o[b, h], _ = attend(qh, k[b, h // G], v[b, h // G], live[b, h], scale)
     return o
 
 
 def mzref_decode_append(dtype: str, q_bits, k_new_bits, v_new_bits, k_cache_bits, v_cache_bits, lens, *,
-                        mask=None, scale: float = 0.0, rope_base: float = 0.0, rope_style: str = "interleaved"):
+                        mask=None, scale: float = 0.0, rope_base: float = 0.0, rope_style: str = "interleaved",
+                        rope_precision: str = "exact", rope_factors=None, rope_mscale: float = 1.0):
     """Oracle of one generation step that appends its own keys and values
     to the static cache and reads the filled length from the cache state
     instead of the host (VoxCPM page, 'Memory and speed': every patch waits
@@ -366,13 +420,13 @@ def mzref_decode_append(dtype: str, q_bits, k_new_bits, v_new_bits, k_cache_bits
             continue
         pos = L + np.arange(T)
         for hk in range(Hkv):
-            kr = rope(kn[b, hk], pos, rope_base, rope_style) if rope_base > 0 else kn[b, hk]
+            kr = rope(kn[b, hk], pos, rope_base, rope_style, rope_precision, rope_factors, rope_mscale) if rope_base > 0 else kn[b, hk]
             k_rows[b, hk] = kr
             k[b, hk, L:L + T] = kr
             v[b, hk, L:L + T] = vn[b, hk]
         causal = np.arange(C)[None, :] <= pos[:, None]          # [T, C]
         for h in range(Hq):
-            qh = rope(q[b, h], pos, rope_base, rope_style) if rope_base > 0 else q[b, h]
+            qh = rope(q[b, h], pos, rope_base, rope_style, rope_precision, rope_factors, rope_mscale) if rope_base > 0 else q[b, h]
             o[b, h], _ = attend(qh, k[b, h // G], v[b, h // G], causal & m[b, h], scale)
     return o, k_rows, overflow
 

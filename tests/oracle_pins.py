@@ -535,6 +535,69 @@ def pin_append_overflow():
     assert np.all(o[1] == 0) and np.all(np.abs(o[0]) > 0)
 
 
+def pin_longrope_vs_transformers():
+    """LongRoPE factors and attention factor: cos / sin of the oracle with
+    factors and mscale equal transformers' longrope inverse frequencies
+    (short and long factor lists) and attention factor applied to
+    cos / sin (library routine, not used by the oracle)."""
+    import warnings
+    from transformers import LlamaConfig
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    D, base = 128, 1e4
+    rng = np.random.default_rng(41)
+    sf = list(1.0 + rng.random(D // 2))
+    lf = list(1.0 + 8.0 * rng.random(D // 2))
+    cfg = LlamaConfig(hidden_size=4 * D, num_attention_heads=4, head_dim=D, max_position_embeddings=32768,
+                      rope_parameters={"rope_type": "longrope", "rope_theta": base, "long_factor": lf,
+                                       "short_factor": sf, "original_max_position_embeddings": 4096})
+    pos = rng.integers(0, 30000, size=50)
+    for seq_len, fac in ((None, sf), (10000, lf)):
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            inv, att = ROPE_INIT_FUNCTIONS["longrope"](cfg, device="cpu", seq_len=seq_len)
+        inv = inv.double().numpy()
+        c, s_ = mzref.rope_cos_sin(pos, D, base, "exact", np.array(fac), att)
+        ang = pos[:, None].astype(np.float64) * inv[None, :]
+        # transformers forms inv_freq in fp32: compare at fp32 resolution of the angle
+        _close(c, np.cos(ang) * att, 2e-7 * 30000, "longrope cos")
+        _close(s_, np.sin(ang) * att, 2e-7 * 30000, "longrope sin")
+        assert att > 1.0
+
+
+def pin_rope_fp16_angles_vs_torch():
+    """fp16 angles: torch half tensors (inv_freq cast to fp16, positions as
+    fp16, their product and its cos / sin in fp16) give the oracle's
+    cos / sin; positions past 2048 round in fp16, so they differ from the
+    exact angles."""
+    D, base = 64, 1e4
+    pos = np.arange(0, 4000, 7)
+    inv = torch.from_numpy(mzref.rope_inv_freq(D, base)).half()
+    t = torch.from_numpy(pos.astype(np.float64)).half()
+    freqs = t[:, None] * inv[None, :]
+    c_ref, s_ref = freqs.cos().double().numpy(), freqs.sin().double().numpy()
+    c, s_ = mzref.rope_cos_sin(pos, D, base, "fp16")
+    ulp = 2.0 ** -10
+    assert np.all(np.abs(c - c_ref) <= ulp) and np.all(np.abs(s_ - s_ref) <= ulp)
+    assert np.mean(c == c_ref) > 0.99 and np.mean(s_ == s_ref) > 0.99
+    ce, _ = mzref.rope_cos_sin(pos, D, base, "exact")
+    assert np.max(np.abs(ce - c)) > 0.05   # the fp16 angles are far off at large positions
+
+
+def pin_rope_bf16_table_vs_torch():
+    """bf16 table: fp32 angles, fp32 cos / sin times mscale, rounded to
+    bf16 by torch equal the oracle's table."""
+    D, base, mscale = 128, 1e6, 1.25
+    pos = np.arange(0, 8192, 3)
+    inv = torch.from_numpy(mzref.rope_inv_freq(D, base)).float()
+    t = torch.from_numpy(pos.astype(np.float32))
+    ang = t[:, None] * inv[None, :]
+    c_ref = (ang.double().cos().float() * mscale).to(torch.bfloat16).double().numpy()
+    s_ref = (ang.double().sin().float() * mscale).to(torch.bfloat16).double().numpy()
+    c, s_ = mzref.rope_cos_sin(pos, D, base, "bf16_table", None, mscale)
+    assert np.array_equal(c, c_ref) and np.array_equal(s_, s_ref)
+    assert np.array_equal(mzref.round_bf16(c_ref), c_ref)
+
+
 ALL_PINS = [
     pin_fp16_decode, pin_bf16_decode, pin_fp32_decode,
     pin_rope_complex_form, pin_rope_hand_values, pin_rope_properties,
@@ -546,4 +609,5 @@ ALL_PINS = [
     pin_rope_half_split_vs_transformers, pin_rope_styles_differ_by_permutation,
     pin_append_empty_cache_is_causal_sdpa, pin_append_single_token_first_row,
     pin_append_equals_sdpa_on_updated_cache, pin_append_overflow,
+    pin_longrope_vs_transformers, pin_rope_fp16_angles_vs_torch, pin_rope_bf16_table_vs_torch,
 ]

@@ -19,7 +19,7 @@ MUTANTS = {
     "rope_sign": ("out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
     "rope_half_split": ("x0, x1 = x[..., 0::2], x[..., 1::2]", "x0, x1 = x[..., :D // 2], x[..., D // 2:]"),
     "rope_freq_no_2": ("np.power(float(base), -2.0 * i / head_dim)", "np.power(float(base), -1.0 * i / head_dim)"),
-    "rope_k_unrotated": ("kh = rope(kh, pk[b], rope_base, rope_style)", "kh = kh"),
+    "rope_k_unrotated": ("kh = rope(kh, pk[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)", "kh = kh"),
     "rope_partial_off_by_one": ("min(pe_attn_head, n_heads_q)", "min(pe_attn_head + 1, n_heads_q)"),
     "gqa_modulo": ("hk = h // G", "hk = h % Hkv"),
     "scale_inverted": ("if scale <= 0:\n        scale = 1.0 / math.sqrt(D)\n    n_rot",
@@ -36,7 +36,7 @@ MUTANTS = {
                                 "live = (sq[:, :, None] == sk[:, None, :])"),
     "segment_pos_no_restart": ("            start = i\n", "            pass\n"),
     "decode_span_inclusive": ("in_span = np.arange(C) < span", "in_span = np.arange(C) <= span"),
-    "decode_q_rope_dropped": ("qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style)", "qh = qh"),
+    "decode_q_rope_dropped": ("qh = rope(qh, np.asarray(q_pos)[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)", "qh = qh"),
     "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "fp16_bias": ("(e - 15)", "(e - 14)"),
     "fp16_subnormal": ("sub = np.ldexp(f, -24)", "sub = np.ldexp(f, -23)"),
@@ -44,8 +44,8 @@ MUTANTS = {
     "half_split_sign": ("out[..., :D // 2] = x0 * c - x1 * s", "out[..., :D // 2] = x0 * c + x1 * s"),
     "half_split_as_interleaved": ("x0, x1 = x[..., :D // 2], x[..., D // 2:]",
                                   "x0, x1 = x[..., 0::2], x[..., 1::2]"),
-    "half_split_style_ignored": ("    if style == \"half\":\n        return rope_half_split(x, pos, base)",
-                                 "    if style == \"half\":\n        return rope_interleaved(x, pos, base)"),
+    "half_split_style_ignored": ("    if style == \"half\":\n        return rope_half_split(x, pos, base, precision, factors, mscale)",
+                                 "    if style == \"half\":\n        return rope_interleaved(x, pos, base, precision, factors, mscale)"),
     "causal_strict": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                       "live = np.arange(Sk)[None, :] < np.arange(Sq)[:, None]"),
     "causal_bottom_right": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
@@ -53,10 +53,17 @@ MUTANTS = {
     "append_causal_strict": ("causal = np.arange(C)[None, :] <= pos[:, None]",
                              "causal = np.arange(C)[None, :] < pos[:, None]"),
     "append_pos_off_by_one": ("pos = L + np.arange(T)", "pos = L + 1 + np.arange(T)"),
-    "append_key_unrotated": ("kr = rope(kn[b, hk], pos, rope_base, rope_style) if rope_base > 0 else kn[b, hk]",
+    "append_key_unrotated": ("kr = rope(kn[b, hk], pos, rope_base, rope_style, rope_precision, rope_factors, rope_mscale) if rope_base > 0 else kn[b, hk]",
                              "kr = kn[b, hk]"),
     "append_values_not_written": ("v[b, hk, L:L + T] = vn[b, hk]", "pass"),
     "append_overflow_inclusive": ("if L < 0 or L + T > C:", "if L < 0 or L + T >= C:"),
+    "longrope_factor_multiplies": ("theta = theta / np.asarray(factors, dtype=np.float64)",
+                                   "theta = theta * np.asarray(factors, dtype=np.float64)"),
+    "longrope_mscale_dropped": ("return np.cos(ang) * mscale, np.sin(ang) * mscale", "return np.cos(ang), np.sin(ang)"),
+    "fp16_positions_exact": ("p16 = p.astype(np.float16).astype(np.float64)", "p16 = p"),
+    "fp16_angle_unrounded": ("a16 = (p16 * th16).astype(np.float16).astype(np.float64)", "a16 = p16 * th16"),
+    "bf16_rounding_truncates": ("r = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))",
+                                "r = (b >> np.uint64(16))"),
     "causal_transposed": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                           "live = np.arange(Sk)[None, :] >= np.arange(Sq)[:, None]"),
 }
