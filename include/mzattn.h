@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MZATTN_VERSION 200 /* major * 10000 + minor * 100 + patch */
+#define MZATTN_VERSION 300 /* major * 10000 + minor * 100 + patch */
 
 /* ---- status codes ------------------------------------------------------ */
 #define MZ_OK 0
@@ -101,6 +101,22 @@ typedef enum mz_mask_kind {
  *   x-transformers style); 1 = half split, pair i is (x[i], x[i+D/2]) (the
  *   "rotate half" layout of Llama-family models).  Other values:
  *   MZ_ERR_VALUE.
+ * rope_factors: optional device fp32 [head_dim/2]; pair i then rotates by
+ *   pos * theta_i / rope_factors[i] (LongRoPE's per-dimension rescaling,
+ *   the MiniCPM-4 LM of the VoxCPM page, "How it works").  NULL = 1.
+ * rope_mscale: cosines and sines are multiplied by it (LongRoPE's
+ *   attention factor); 0 = 1.
+ * rope_precision: how the cosines and sines are formed.
+ *   0 = exact: the angle in fp64, cos and sin to fp32 (the default);
+ *   1 = fp16 angles: theta_i and the position rounded to fp16, their
+ *       product rounded to fp16, its cos and sin rounded to fp16 (the F5-TTS
+ *       page, "What matches upstream": on GPU the model runs in fp16 and so
+ *       do inv_freq and the angles);
+ *   2 = bf16 table: angle pos * fp32(theta_i) in fp32, cos and sin in fp32
+ *       times rope_mscale, rounded to bf16 (the VoxCPM page: the LongRoPE
+ *       table is built in fp32 and rounded with the model to bf16).
+ *   Other values: MZ_ERR_VALUE.  The same fields, with the same meaning,
+ *   are in mzattn_decode_args and mzattn_decode_append_args.
  * pe_attn_head: < 0 rotates every head; n >= 0 rotates query heads 0..n-1
  *   and the K heads they read.  With GQA only "none" (0) or "all" (< 0 or
  *   >= heads_q) is accepted (MZ_ERR_UNSUPPORTED otherwise).
@@ -126,6 +142,9 @@ typedef struct mzattn_fwd_args {
   float scale;
   int32_t rope_style;   /* 0 interleaved, 1 half split */
   double rope_base;
+  int32_t rope_precision;     /* 0 exact, 1 fp16 angles, 2 bf16 table */
+  float rope_mscale;          /* cos / sin scale; 0 = 1 */
+  const float* rope_factors;  /* optional device [head_dim/2], NULL = 1 */
   const void* q;
   const void* k;
   const void* v;
@@ -212,6 +231,9 @@ typedef struct mzattn_decode_args {
   float scale;
   int32_t rope_style;   /* 0 interleaved, 1 half split */
   double rope_base;
+  int32_t rope_precision;     /* 0 exact, 1 fp16 angles, 2 bf16 table */
+  float rope_mscale;          /* cos / sin scale; 0 = 1 */
+  const float* rope_factors;  /* optional device [head_dim/2], NULL = 1 */
   const void* q;
   int64_t q_stride[3];
   const void* k_cache;
@@ -278,6 +300,9 @@ typedef struct mzattn_decode_append_args {
   float scale;
   int32_t rope_style;   /* 0 interleaved, 1 half split */
   double rope_base;     /* 0: no rotation */
+  int32_t rope_precision;     /* 0 exact, 1 fp16 angles, 2 bf16 table */
+  float rope_mscale;          /* cos / sin scale; 0 = 1 */
+  const float* rope_factors;  /* optional device [head_dim/2], NULL = 1 */
   const void* q;
   int64_t q_stride[3];
   const void* k_new;

@@ -39,6 +39,25 @@ def _rope_style(style) -> int:
         raise MzattnError(MZ_ERR_VALUE, f"rope_style must be one of {sorted(ROPE_STYLES)}")
     return ROPE_STYLES[style]
 
+
+ROPE_PRECISIONS = {"exact": 0, "fp16": 1, "bf16_table": 2}
+
+
+def _set_rope_extra(a, keep, precision, mscale, factors):
+    """rope_precision ('exact' | 'fp16' | 'bf16_table'), rope_mscale and
+    the optional fp32 device tensor of LongRoPE factors [head_dim / 2]."""
+    if precision not in ROPE_PRECISIONS:
+        raise MzattnError(MZ_ERR_VALUE, f"rope_precision must be one of {sorted(ROPE_PRECISIONS)}")
+    a.rope_precision = ROPE_PRECISIONS[precision]
+    a.rope_mscale = float(mscale)
+    if factors is not None:
+        torch = _torch()
+        if factors.dtype != torch.float32 or factors.dim() != 1 or factors.shape[0] != a.head_dim // 2 \
+                or not factors.is_contiguous():
+            raise MzattnError(MZ_ERR_SHAPE, "rope_factors must be a contiguous float32 tensor [head_dim / 2]")
+        a.rope_factors = factors.data_ptr()
+        keep.append(factors)
+
 _i64x3 = ctypes.c_int64 * 3
 _i64x4 = ctypes.c_int64 * 4
 
@@ -68,6 +87,9 @@ class FwdArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("rope_precision", ctypes.c_int32),
+        ("rope_mscale", ctypes.c_float),
+        ("rope_factors", ctypes.c_void_p),
         ("q", ctypes.c_void_p),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
@@ -106,6 +128,9 @@ class DecodeArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("rope_precision", ctypes.c_int32),
+        ("rope_mscale", ctypes.c_float),
+        ("rope_factors", ctypes.c_void_p),
         ("q", ctypes.c_void_p),
         ("q_stride", _i64x3),
         ("k_cache", ctypes.c_void_p),
@@ -136,6 +161,9 @@ class DecodeAppendArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("rope_precision", ctypes.c_int32),
+        ("rope_mscale", ctypes.c_float),
+        ("rope_factors", ctypes.c_void_p),
         ("q", ctypes.c_void_p),
         ("q_stride", _i64x3),
         ("k_new", ctypes.c_void_p),
@@ -305,8 +333,8 @@ class FwdCall:
 
     def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
-                 rope_style: str = "interleaved",
-                 out=None, return_lse: bool = False, workspace=None, stream=None):
+                 rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
+                 rope_factors=None, out=None, return_lse: bool = False, workspace=None, stream=None):
         torch = _torch()
         L = lib()
         B, Hq, Sq, D = q.shape
@@ -325,6 +353,7 @@ class FwdCall:
         a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k, "k")
         a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
         keep = [q, k, v, o]
+        _set_rope_extra(a, keep, rope_precision, rope_mscale, rope_factors)
         if (mask is not None) + (seg_q is not None) + bool(causal) > 1:
             raise MzattnError(MZ_ERR_UNSUPPORTED, "give at most one of mask, segment ids, causal")
         if causal:
@@ -398,15 +427,16 @@ class FwdCall:
 
 def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
-               rope_style: str = "interleaved",
-               out=None, return_lse: bool = False, workspace=None, stream=None):
+               rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
+               rope_factors=None, out=None, return_lse: bool = False, workspace=None, stream=None):
     """Masked bidirectional attention forward (see ``mzattn_fwd`` in
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
     same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
     [B, S] (segment mode); causal: key j live for query i iff j <= i.
     Returns o (and lse when ``return_lse``)."""
     return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, causal=causal, pos_q=pos_q, pos_k=pos_k,
-                   scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, out=out,
+                   scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, rope_precision=rope_precision,
+                   rope_mscale=rope_mscale, rope_factors=rope_factors, out=out,
                    return_lse=return_lse, workspace=workspace, stream=stream)()
 
 
@@ -416,7 +446,8 @@ class DecodeCall:
     shape, strides and dtype; ``__call__`` launches on the call's stream."""
 
     def __init__(self, q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
-                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved", out=None,
+                 scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
+                 rope_precision: str = "exact", rope_mscale: float = 0.0, rope_factors=None, out=None,
                  workspace=None, stream=None):
         torch = _torch()
         L = lib()
@@ -436,6 +467,7 @@ class DecodeCall:
         a.q_stride, a.k_stride = _strides3(q, "q"), _strides3(k_cache, "k_cache")
         a.v_stride, a.o_stride = _strides3(v_cache, "v_cache"), _strides3(o, "o")
         keep = [q, k_cache, v_cache, o]
+        _set_rope_extra(a, keep, rope_precision, rope_mscale, rope_factors)
         if mask is not None:
             m, st = _mask_strides(mask, B, Hq, T, C)
             a.mask, a.mask_stride = m.data_ptr(), st
@@ -470,13 +502,14 @@ class DecodeCall:
 
 def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
                   scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
-                  out=None, workspace=None, stream=None):
+                  rope_precision: str = "exact", rope_mscale: float = 0.0, rope_factors=None, out=None, workspace=None, stream=None):
     """One static-cache step (see ``mzattn_decode`` in include/mzattn.h).
     q [B, Hq, q_len, D]; k_cache / v_cache [B, Hkv, cache_len, D]; keys
     [0, span) considered (default: the whole cache); mask: bool
     [B|1, Hq|1, q_len|1, cache_len] or None."""
     return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
-                      q_pos=q_pos, rope_style=rope_style, out=out, workspace=workspace, stream=stream)()
+                      q_pos=q_pos, rope_style=rope_style, rope_precision=rope_precision,
+                      rope_mscale=rope_mscale, rope_factors=rope_factors, out=out, workspace=workspace, stream=stream)()
 
 
 class DecodeAppendCall:
@@ -491,7 +524,8 @@ class DecodeAppendCall:
     does not fit."""
 
     def __init__(self, q, k_new, v_new, k_cache, v_cache, length, *, mask=None, scale: float = 0.0,
-                 rope_base: float = 0.0, rope_style: str = "interleaved", overflow=None, out=None,
+                 rope_base: float = 0.0, rope_style: str = "interleaved", rope_precision: str = "exact",
+                 rope_mscale: float = 0.0, rope_factors=None, overflow=None, out=None,
                  workspace=None, stream=None):
         torch = _torch()
         L = lib()
@@ -516,6 +550,7 @@ class DecodeAppendCall:
         a.len = length.data_ptr()
         a.len_stride_b = length.stride(0) if length.shape[0] > 1 else 0
         keep = [q, k_new, v_new, k_cache, v_cache, length, o]
+        _set_rope_extra(a, keep, rope_precision, rope_mscale, rope_factors)
         if mask is not None:
             m, st = _mask_strides(mask, B, Hq, T, C)
             a.mask, a.mask_stride = m.data_ptr(), st
@@ -540,10 +575,12 @@ class DecodeAppendCall:
 
 
 def mzattn_decode_append(q, k_new, v_new, k_cache, v_cache, length, *, mask=None, scale: float = 0.0,
-                         rope_base: float = 0.0, rope_style: str = "interleaved", overflow=None, out=None,
+                         rope_base: float = 0.0, rope_style: str = "interleaved", rope_precision: str = "exact",
+                         rope_mscale: float = 0.0, rope_factors=None, overflow=None, out=None,
                          workspace=None, stream=None):
     """One append step (see ``DecodeAppendCall``): writes the new rows into
     the caches and returns o [B, Hq, q_len, D]."""
     return DecodeAppendCall(q, k_new, v_new, k_cache, v_cache, length, mask=mask, scale=scale,
-                            rope_base=rope_base, rope_style=rope_style, overflow=overflow, out=out,
+                            rope_base=rope_base, rope_style=rope_style, rope_precision=rope_precision,
+                            rope_mscale=rope_mscale, rope_factors=rope_factors, overflow=overflow, out=out,
                             workspace=workspace, stream=stream)()

@@ -40,6 +40,24 @@ size_t elem_size(int dtype) { return dtype == MZ_F32 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// rope_precision, rope_mscale and rope_factors (checked whether or not
+// rotation is on, so a bad value never passes silently)
+int check_rope_extra(int32_t precision, float mscale, const float* factors) {
+  if (precision < 0 || precision > 2) return fail(MZ_ERR_VALUE, "rope_precision must be 0, 1 or 2 (got %d)", precision);
+  if (!isfinite(mscale) || mscale < 0.f) return fail(MZ_ERR_VALUE, "rope_mscale must be finite and >= 0");
+  if (factors != nullptr && !aligned(factors, 4)) return fail(MZ_ERR_ALIGN, "rope_factors is not 4-byte aligned");
+  return MZ_OK;
+}
+
+mz::RopeSpec rope_spec(double base, int32_t precision, float mscale, const float* factors) {
+  mz::RopeSpec r;
+  r.log2_base = base > 0.0 ? log2(base) : 0.0;
+  r.factors = factors;
+  r.mscale = mscale > 0.f ? mscale : 1.f;
+  r.precision = precision;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // forward plan
 // ---------------------------------------------------------------------------
@@ -91,6 +109,10 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
     return fail(MZ_ERR_VALUE, "rope_base must be finite and >= 0");
   if (a->rope_base > 0.0 && a->rope_base == 1.0)
     return fail(MZ_ERR_VALUE, "rope_base 1 gives no frequencies");
+  {
+    const int st = check_rope_extra(a->rope_precision, a->rope_mscale, a->rope_factors);
+    if (st != MZ_OK) return st;
+  }
 
   const int Hq = a->heads_q, Hkv = a->heads_kv, G = Hq / Hkv;
   int n_rot = 0;
@@ -221,6 +243,10 @@ int plan_decode(const mzattn_decode_args* a, DecPlan* pl) {
   if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
   if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
     return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
+  {
+    const int st = check_rope_extra(a->rope_precision, a->rope_mscale, a->rope_factors);
+    if (st != MZ_OK) return st;
+  }
   if (a->rope_style != 0 && a->rope_style != 1)
     return fail(MZ_ERR_VALUE, "rope_style must be 0 or 1 (got %d)", a->rope_style);
   pl->R = G * a->q_len;
@@ -297,7 +323,7 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   p.n_rot = pl.n_rot; p.n_rot_kv = pl.n_rot_kv;
   p.rope_style = a->rope_style;
   if (pl.n_rot > 0) {
-    p.log2_base = log2(a->rope_base);
+    p.rs = rope_spec(a->rope_base, a->rope_precision, a->rope_mscale, a->rope_factors);
     p.rope_tab = reinterpret_cast<float2*>(ws + pl.off_tab);
     p.rope_tab_len = pl.tab_len;
     if (a->pos_q) { p.pos_q_mode = mz::POS_ARRAY; p.pos_q = a->pos_q; p.pos_q_sb = a->pos_q_stride_b; }
@@ -433,7 +459,7 @@ int mzattn_decode(const mzattn_decode_args* a, void* stream) {
   if (a->rope_base > 0.0) {
     p.rope = 1;
     p.rope_style = a->rope_style;
-    p.log2_base = log2(a->rope_base);
+    p.rs = rope_spec(a->rope_base, a->rope_precision, a->rope_mscale, a->rope_factors);
     p.q_in = a->q;
     for (int i = 0; i < 3; ++i) p.q_in_s[i] = a->q_stride[i];
     p.q_pos = a->q_pos; p.q_pos_sb = a->q_pos_stride_b;
@@ -486,7 +512,9 @@ int validate_append_full(const mzattn_decode_append_args* a, mzattn_decode_args*
   if (a->dtype == MZ_F32) return fail(MZ_ERR_UNSUPPORTED, "mzattn_decode_append supports bf16 and fp16");
   if (!isfinite(a->rope_base) || a->rope_base < 0.0 || a->rope_base == 1.0)
     return fail(MZ_ERR_VALUE, "rope_base must be finite, >= 0 and != 1");
-  int st = validate_decode_full(d, pl);
+  int st = check_rope_extra(a->rope_precision, a->rope_mscale, a->rope_factors);
+  if (st != MZ_OK) return st;
+  st = validate_decode_full(d, pl);
   if (st != MZ_OK || pl->empty) return st;
   if (a->cache_len < 1) return fail(MZ_ERR_SHAPE, "cache_len must be >= 1 to append");
   if (a->k_new == nullptr || a->v_new == nullptr) return fail(MZ_ERR_NULL, "k_new and v_new must not be NULL");
@@ -546,7 +574,7 @@ int mzattn_decode_append(const mzattn_decode_append_args* a, void* stream) {
   if (a->rope_base > 0.0) {
     p.rope = 1;
     p.rope_style = a->rope_style;
-    p.log2_base = log2(a->rope_base);
+    p.rs = rope_spec(a->rope_base, a->rope_precision, a->rope_mscale, a->rope_factors);
   }
   p.k = a->k_cache; p.v = a->v_cache; p.o = a->o;
   p.k_w = a->k_cache; p.v_w = a->v_cache;

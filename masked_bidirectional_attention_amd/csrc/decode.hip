@@ -33,7 +33,7 @@ __global__ void decode_q_rotate16_kernel(const DecodeParams p) {
   const int h = (int)((row / p.T) % p.Hq);
   const int b = (int)(row / ((int64_t)p.T * p.Hq));
   const uint16_t* src = (const uint16_t*)p.q_in + b * p.q_in_s[0] + h * p.q_in_s[1] + (int64_t)t * p.q_in_s[2];
-  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
+  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.rs);
   if (p.rope_style == 1) {
     // half split: pair (i, i + D/2)
     const float a = Elem<T>::to_f32(src[i]), c = Elem<T>::to_f32(src[i + half]);
@@ -63,7 +63,7 @@ __global__ void decode_q_rotate32_kernel(const DecodeParams p) {
   // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
   const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
   const float2 x = make_float2(src[d0], src[d1]);
-  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.log2_base);
+  const float2 cs = rope_cs_direct(p.q_pos[b * p.q_pos_sb + t], i, p.D, p.rs);
   float* dst = (float*)p.q + row * p.D;
   dst[d0] = fmaf(x.x, cs.x, -x.y * cs.y);
   dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     // q at len + t (its loads came first: this overlaps the K/V loads)
     if (p.rope) {
       for (int idx = tid; idx < p.T * (D / 2); idx += 256)
-        cs_s[idx / (D / 2)][idx % (D / 2)] = rope_cs_direct(lenb + idx / (D / 2), idx % (D / 2), D, p.log2_base);
+        cs_s[idx / (D / 2)][idx % (D / 2)] = rope_cs_direct(lenb + idx / (D / 2), idx % (D / 2), D, p.rs);
       __syncthreads();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {

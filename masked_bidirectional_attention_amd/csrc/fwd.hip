@@ -15,15 +15,15 @@ namespace mz {
 // ---------------------------------------------------------------------------
 // Prepass 1: cos/sin table of the rotary angles, positions [0, len).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int len, int D, double log2_base) {
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int len, int D, const RopeSpec rs) {
   __shared__ double theta[64];
   const int half = D / 2;
-  if (threadIdx.x < half) theta[threadIdx.x] = rope_theta(threadIdx.x, D, log2_base);
+  if (threadIdx.x < half) theta[threadIdx.x] = rope_theta(threadIdx.x, D, rs);
   __syncthreads();
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)len * half) return;
   const int pos = (int)(idx / half), i = (int)(idx % half);
-  tab[idx] = rope_cs_theta(pos, theta[i]);
+  tab[idx] = rope_cs_theta(pos, theta[i], rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   uint16_t* dst = (uint16_t*)p.k_rot + row * p.D + d0;
   const int pos = key_position(p, b, j);
   if constexpr (!HALF) {
-    *(uint4*)dst = rope_quad<T>(*(const uint4*)src, p.rope_tab, p.rope_tab_len, pos, d0, p.D, p.log2_base);
+    *(uint4*)dst = rope_quad<T>(*(const uint4*)src, p.rope_tab, p.rope_tab_len, pos, d0, p.D, p.rs);
   } else {
     const int hd = p.D / 2;
     const uint4 x0 = *(const uint4*)src, x1 = *(const uint4*)(src + hd);
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
       for (int e = 0; e < 2; ++e) {
         const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
         const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
-        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, d0 + 2 * t + e, p.D, p.log2_base);
+        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, d0 + 2 * t + e, p.D, p.rs);
         r[0][e] = fmaf(a, cs.x, -c * cs.y);
         r[1][e] = fmaf(c, cs.x, a * cs.y);
       }
@@ -225,7 +225,7 @@ __global__ void k_rotate32_kernel(const FwdParams p) {
   const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
   const float* src = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2];
   const float2 x = make_float2(src[d0], src[d1]);
-  const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.log2_base);
+  const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.rs);
   float* dst = (float*)p.k_rot + row * p.D;
   dst[d0] = fmaf(x.x, cs.x, -x.y * cs.y);
   dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           for (int e = 0; e < 2; ++e) {
             const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
             const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
-            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8 + 2 * t + e, D, p.log2_base);
+            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8 + 2 * t + e, D, p.rs);
             r[0][e] = fmaf(a, cs.x, -c * cs.y);
             r[1][e] = fmaf(c, cs.x, a * cs.y);
           }
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           float a = Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF));
           float c = Elem<T>::to_f32((uint16_t)(wv[t] >> 16));
           if (rot) {
-            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, d0 / 2 + t, D, p.log2_base);
+            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, d0 / 2 + t, D, p.rs);
             const float ra = fmaf(a, cs.x, -c * cs.y);
             const float rc = fmaf(c, cs.x, a * cs.y);
             a = ra;
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
       const int d0 = half ? i : 2 * i, d1 = half ? i + D / 2 : 2 * i + 1;
       float2 x = qvalid ? make_float2(qrow[d0], qrow[d1]) : make_float2(0.f, 0.f);
       if (rot && qvalid) {
-        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, i, D, p.log2_base);
+        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, i, D, p.rs);
         const float a = fmaf(x.x, cs.x, -x.y * cs.y);
         const float c = fmaf(x.y, cs.x, x.x * cs.y);
         x = make_float2(a, c);
@@ -1051,7 +1051,7 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
   if (p.n_rot > 0 && p.rope_tab_len > 0) {
     const int64_t n = (int64_t)p.rope_tab_len * (p.D / 2);
     rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p.rope_tab, p.rope_tab_len, p.D,
-                                                                              p.log2_base);
+                                                                              p.rs);
   }
   if (p.mask_kind == 2) {
     const int nkb = (p.Sk + 255) / 256;

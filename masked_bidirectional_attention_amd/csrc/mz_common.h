@@ -7,6 +7,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "mz_internal.h"
+
 namespace mz {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -174,45 +176,70 @@ __device__ inline float half_swap_sum(float x) {
 }
 
 // ---- rotary embedding angles -----------------------------------------------
-// theta_i = base^(-2i/D) in fp64.  The angle pos * theta_i is formed in fp64
+// theta_i = base^(-2i/D) / factor_i in fp64 (factor_i = 1 without LongRoPE
+// factors).  Exact (precision 0): the angle pos * theta_i is formed in fp64
 // and reduced to [-pi, pi] by subtracting the nearest multiple of 2 pi (2 pi
 // split in two doubles, Cody-Waite), then its sine and cosine are taken in
-// fp32 (accurate to about one fp32 ulp on the reduced range).  The table
+// fp32 (accurate to about one fp32 ulp on the reduced range) and multiplied
+// by mscale.  fp16 angles (1): theta_i and pos rounded to fp16, their
+// product (exact in fp32) rounded to fp16, cos and sin of it (fp64)
+// rounded to fp16, times mscale.  bf16 table (2): the angle pos *
+// fp32(theta_i) rounded to fp32, cos and sin (fp64) rounded to fp32, times
+// mscale, rounded to bf16.  The table
 // holds positions [0, tab_len); other positions take the same formula
 // directly, so both routes give identical bits.
-__device__ inline double rope_theta(int i, int D, double log2_base) {
-  return exp2(-(double)(2 * i) / (double)D * log2_base);
+__device__ inline double rope_theta(int i, int D, const RopeSpec& r) {
+  const double th = exp2(-(double)(2 * i) / (double)D * r.log2_base);
+  return r.factors != nullptr ? th / (double)r.factors[i] : th;
 }
-__device__ inline float2 rope_cs_theta(int pos, double theta) {
+__device__ inline float2 rope_cs_theta(int pos, double theta, const RopeSpec& r) {
+  float s, c;
+  // (the rounding of cos / sin to fp16 or bf16 is taken from their fp64
+  // values, so it does not depend on the fp32 routine's last bit)
+  if (r.precision == 1) {
+    const float th16 = (float)(_Float16)theta;
+    const float p16 = (float)(_Float16)(float)pos;
+    const float a16 = (float)(_Float16)(p16 * th16);  // exact product, one rounding to fp16
+    double sd, cd;
+    sincos((double)a16, &sd, &cd);
+    c = (float)(_Float16)cd;
+    s = (float)(_Float16)sd;
+    return make_float2(c * r.mscale, s * r.mscale);
+  }
+  if (r.precision == 2) {
+    const float a32 = (float)pos * (float)theta;
+    double sd, cd;
+    sincos((double)a32, &sd, &cd);
+    const __bf16 cb = (__bf16)((float)cd * r.mscale), sb = (__bf16)((float)sd * r.mscale);
+    return make_float2((float)cb, (float)sb);
+  }
   const double ang = (double)pos * theta;
   const double k = rint(ang * 0.15915494309189533577);  // 1 / (2 pi)
-  double r = fma(-k, 6.28318530717958623200, ang);     // 2 pi, high part
-  r = fma(-k, 2.44929359829470635445e-16, r);           // 2 pi, low part
-  float s, c;
-  sincosf((float)r, &s, &c);
-  return make_float2(c, s);
+  double rr = fma(-k, 6.28318530717958623200, ang);    // 2 pi, high part
+  rr = fma(-k, 2.44929359829470635445e-16, rr);         // 2 pi, low part
+  sincosf((float)rr, &s, &c);
+  return make_float2(c * r.mscale, s * r.mscale);
 }
-__device__ inline float2 rope_cs_direct(int pos, int i, int D, double log2_base) {
-  return rope_cs_theta(pos, rope_theta(i, D, log2_base));
+__device__ inline float2 rope_cs_direct(int pos, int i, int D, const RopeSpec& r) {
+  return rope_cs_theta(pos, rope_theta(i, D, r), r);
 }
 
-__device__ inline float2 rope_cs(const float2* tab, int tab_len, int pos, int i, int D,
-                                 double log2_base) {
+__device__ inline float2 rope_cs(const float2* tab, int tab_len, int pos, int i, int D, const RopeSpec& r) {
   if (pos >= 0 && pos < tab_len) return tab[(size_t)pos * (D / 2) + i];
-  return rope_cs_direct(pos, i, D, log2_base);
+  return rope_cs_direct(pos, i, D, r);
 }
 
 // Rotate the 8 consecutive elements held in a quad (d0 even) in fp32 and
 // round back to the storage type.
 template <typename T>
 __device__ inline uint4 rope_quad(uint4 x, const float2* tab, int tab_len, int pos, int d0, int D,
-                                  double log2_base) {
+                                  const RopeSpec& r) {
   uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float a = Elem<T>::to_f32((uint16_t)(w[t] & 0xFFFF));
     float b = Elem<T>::to_f32((uint16_t)(w[t] >> 16));
-    float2 cs = rope_cs(tab, tab_len, pos, d0 / 2 + t, D, log2_base);
+    float2 cs = rope_cs(tab, tab_len, pos, d0 / 2 + t, D, r);
     float ra = fmaf(a, cs.x, -b * cs.y);
     float rb = fmaf(b, cs.x, a * cs.y);
     w[t] = Elem<T>::pack2(ra, rb);

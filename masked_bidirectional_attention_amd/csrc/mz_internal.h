@@ -16,6 +16,16 @@ constexpr int F32_BN = 32;
 // Decode: keys per chunk (fixed, aligned to key index 0).
 constexpr int DEC_CHUNK = 128;
 
+// Rotary embedding: base, optional per-pair factors (LongRoPE), scale of
+// cos / sin, and how cos / sin are formed (0 exact, 1 fp16 angles, 2 bf16
+// table).
+struct RopeSpec {
+  double log2_base;
+  const float* factors;  // [D/2] (device) or nullptr
+  float mscale;          // 1 when not given
+  int precision;
+};
+
 enum PosMode { POS_ARANGE = 0, POS_ARRAY = 1, POS_SEGMENT = 2 };
 
 struct FwdParams {
@@ -31,7 +41,7 @@ struct FwdParams {
   // rotary embedding
   int n_rot, n_rot_kv;
   int rope_style;  // 0 interleaved (2i, 2i+1), 1 half split (i, i + D/2)
-  double log2_base;
+  RopeSpec rs;
   int pos_q_mode, pos_k_mode;
   const int32_t* pos_q;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
   int64_t pos_q_sb;
@@ -80,7 +90,7 @@ struct DecodeParams {
   int64_t q_in_s[3];
   const int32_t* q_pos;
   int64_t q_pos_sb;
-  double log2_base;
+  RopeSpec rs;
   int rope;
   int rope_style;  // 0 interleaved, 1 half split
   // append step (mzattn_decode_append): the new tokens' rows come from

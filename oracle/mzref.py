@@ -127,7 +127,9 @@ def rope_cos_sin(pos, head_dim: int, base: float, precision: str = "exact", fact
     precision 'exact': the angle pos * theta_i and its cos / sin in fp64.
     'fp16' (F5-TTS page, 'What matches upstream': on GPU inv_freq and the
     angles are fp16): theta_i and pos rounded to fp16, their product rounded
-    to fp16, cos / sin of it rounded to fp16, then times mscale.
+    to fp16, cos / sin of it rounded to fp16, then times mscale (reading:
+    the rounding is taken from the fp64 cos / sin; torch rounds an fp32
+    one, which lands one fp16 ulp away in rare cases).
     'bf16_table' (VoxCPM page, 'What matches upstream': the LongRoPE table
     is built in fp32 and rounded with the model to bf16): the fp32 product
     of fp32 pos and fp32 theta_i, cos / sin rounded to fp32, times mscale

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.mzattn_version() == 200
+    assert lib.mzattn_version() == 300
     for code in range(0, -11, -1):
         msg = lib.mzattn_strerror(code).decode()
         assert msg and msg != "unknown status", code
@@ -409,3 +409,31 @@ def test_decode_append_rejects(lib, name, edit, code):
     a = good_app()
     edit(a)
     assert vapp(lib, a) == code, (name, lib.mzattn_last_error())
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("rope_precision", 3, B.MZ_ERR_VALUE),
+    ("rope_precision", -1, B.MZ_ERR_VALUE),
+    ("rope_mscale", -1.0, B.MZ_ERR_VALUE),
+    ("rope_mscale", float("nan"), B.MZ_ERR_VALUE),
+    ("rope_factors", FAKE + 2, B.MZ_ERR_ALIGN),
+])
+def test_rope_options_checked_everywhere(lib, field, value, code):
+    """The RoPE precision, scale and factors are checked by all three entry
+    points."""
+    a = good_fwd()
+    setattr(a, field, value)
+    assert vfwd(lib, a) == code, lib.mzattn_last_error()
+    d, _ = good_dec()
+    setattr(d, field, value)
+    assert vdec(lib, d) == code, lib.mzattn_last_error()
+    p = good_app()
+    setattr(p, field, value)
+    assert vapp(lib, p) == code, lib.mzattn_last_error()
+
+
+def test_rope_options_valid(lib):
+    for prec in (0, 1, 2):
+        a = good_fwd()
+        a.rope_precision, a.rope_mscale, a.rope_factors = prec, 1.118, FAKE + 0x6000000
+        assert vfwd(lib, a) == 0, lib.mzattn_last_error()

@@ -559,3 +559,74 @@ def test_decode_append_graph_replay():
         assert np.array_equal(bits(o_graph), bits(o_eager)), f"replay {step}"
         assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"caches after replay {step}"
         length += 1                                  # next position, on the device
+
+
+# --------------------------------------------------------------------------
+# RoPE variants: LongRoPE factors and attention factor; upstream precisions
+# --------------------------------------------------------------------------
+
+_ROPE_VARIANTS = [
+    # precision, with factors, mscale
+    ("fp16", False, 0.0),
+    ("bf16_table", True, 1.118),
+    ("exact", True, 1.25),
+]
+
+
+def _factors(D, seed):
+    return torch.from_numpy((1.0 + 3.0 * np.random.default_rng(seed).random(D // 2)).astype(np.float32))
+
+
+@pytest.mark.parametrize("variant", _ROPE_VARIANTS, ids=lambda v: f"{v[0]}-{'factors' if v[1] else 'nofactors'}")
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_rope_variants_fwd(variant, style, dtype):
+    """Forward with the RoPE options (table route for positions below the
+    table size, the direct route above: segment positions are short, the
+    explicit positions reach 20000)."""
+    prec, with_f, mscale = variant
+    import masked_bidirectional_attention_amd as mz
+    case = W.random_fwd(zlib.crc32(repr(("ropev", prec, style, dtype)).encode()) % 10000, 2, 4, 2, 130, 150,
+                        128 if dtype != "f32" else 64, dtype, W.MASK_BOOL, rope_base=1e4, mask_shape="key")
+    D = case.q.shape[-1]
+    f = _factors(D, 5) if with_f else None
+    rng = np.random.default_rng(6)
+    pq = torch.from_numpy(rng.integers(0, 20000, size=(2, 130)).astype(np.int32))
+    pk = torch.from_numpy(rng.integers(0, 20000, size=(2, 150)).astype(np.int32))
+    o = mz.mzattn_fwd(dev(case.q), dev(case.k), dev(case.v), mask=dev(case.mask), rope_base=1e4, rope_style=style,
+                      pos_q=dev(pq), pos_k=dev(pk), rope_precision=prec, rope_mscale=mscale,
+                      rope_factors=dev(f))
+    torch.cuda.synchronize()
+    ref, _ = mzref.mzref_fwd(dtype, W.to_bits(case.q), W.to_bits(case.k), W.to_bits(case.v), rope_base=1e4,
+                             rope_style=style, pos_q=pq.numpy(), pos_k=pk.numpy(), mask_kind="bool",
+                             mask=case.mask.numpy(), rope_precision=prec,
+                             rope_factors=None if f is None else f.numpy().astype(np.float64),
+                             rope_mscale=mscale if mscale > 0 else 1.0)
+    assert_parity(dtype, o, ref, f"rope {variant} {style}")
+
+
+@pytest.mark.parametrize("variant", _ROPE_VARIANTS, ids=lambda v: f"{v[0]}-{'factors' if v[1] else 'nofactors'}")
+def test_rope_variants_decode_and_append(variant):
+    prec, with_f, mscale = variant
+    import masked_bidirectional_attention_amd as mz
+    f = _factors(128, 7) if with_f else None
+    fo = None if f is None else f.numpy().astype(np.float64)
+    ms = mscale if mscale > 0 else 1.0
+    case = W.random_decode(77, 2, 16, 2, 2, 3000, 128, "bf16", 2500, 2560, rope_base=1e4)
+    o = mz.mzattn_decode(dev(case.q), dev(case.k_cache), dev(case.v_cache), span=case.span, mask=dev(case.mask),
+                         rope_base=1e4, q_pos=dev(case.q_pos), rope_precision=prec, rope_mscale=mscale,
+                         rope_factors=dev(f))
+    torch.cuda.synchronize()
+    ref = mzref.mzref_decode("bf16", W.to_bits(case.q), W.to_bits(case.k_cache), W.to_bits(case.v_cache),
+                             span=case.span, mask=case.mask.numpy(), rope_base=1e4, q_pos=case.q_pos.numpy(),
+                             rope_precision=prec, rope_factors=fo, rope_mscale=ms)
+    assert_parity("bf16", o, ref, f"decode rope {variant}")
+    q, kn, vn, kc, vc, ln, _ = _append_case(78, 2, 16, 2, 2, 3000, 128, "bf16", [2000, 2997])
+    kc_d, vc_d = dev(kc), dev(vc)
+    oa = mz.mzattn_decode_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, dev(ln), rope_base=1e4,
+                                 rope_precision=prec, rope_mscale=mscale, rope_factors=dev(f))
+    torch.cuda.synchronize()
+    refa, k_rows, _ = mzref.mzref_decode_append("bf16", W.to_bits(q), W.to_bits(kn), W.to_bits(vn), W.to_bits(kc),
+                                                W.to_bits(vc), [2000, 2997], rope_base=1e4, rope_precision=prec,
+                                                rope_factors=fo, rope_mscale=ms)
+    assert_parity("bf16", oa, refa, f"append rope {variant}")
