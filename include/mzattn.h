@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MZATTN_VERSION 300 /* major * 10000 + minor * 100 + patch */
+#define MZATTN_VERSION 400 /* major * 10000 + minor * 100 + patch */
 
 /* ---- status codes ------------------------------------------------------ */
 #define MZ_OK 0
@@ -117,6 +117,12 @@ typedef enum mz_mask_kind {
  *       table is built in fp32 and rounded with the model to bf16).
  *   Other values: MZ_ERR_VALUE.  The same fields, with the same meaning,
  *   are in mzattn_decode_args and mzattn_decode_append_args.
+ * q_norm_w / k_norm_w: optional [head_dim] weights in the storage dtype,
+ *   16-byte aligned.  Every q (k) row is first scaled to unit root mean
+ *   square and multiplied by the weight, x / sqrt(mean(x^2) + norm_eps) *
+ *   w, in fp32, before RoPE (the Qwen3 LM of the OmniVoice page normalises
+ *   q and k separately, as transformers does).  NULL: no normalisation.
+ * norm_eps: finite, >= 0 (used when a weight is given).
  * pe_attn_head: < 0 rotates every head; n >= 0 rotates query heads 0..n-1
  *   and the K heads they read.  With GQA only "none" (0) or "all" (< 0 or
  *   >= heads_q) is accepted (MZ_ERR_UNSUPPORTED otherwise).
@@ -158,6 +164,9 @@ typedef struct mzattn_fwd_args {
   const int32_t* seg_q;
   const int32_t* seg_k;
   int64_t seg_q_stride_b, seg_k_stride_b;
+  const void* q_norm_w;   /* optional [head_dim], storage dtype */
+  const void* k_norm_w;   /* optional [head_dim], storage dtype */
+  float norm_eps;
   float* lse;
   void* workspace;
   size_t workspace_bytes;

@@ -108,6 +108,9 @@ class FwdArgs(ctypes.Structure):
         ("seg_k", ctypes.c_void_p),
         ("seg_q_stride_b", ctypes.c_int64),
         ("seg_k_stride_b", ctypes.c_int64),
+        ("q_norm_w", ctypes.c_void_p),
+        ("k_norm_w", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
         ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
@@ -334,7 +337,8 @@ class FwdCall:
     def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                  rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
-                 rope_factors=None, out=None, return_lse: bool = False, workspace=None, stream=None):
+                 rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6,
+                 out=None, return_lse: bool = False, workspace=None, stream=None):
         torch = _torch()
         L = lib()
         B, Hq, Sq, D = q.shape
@@ -354,6 +358,13 @@ class FwdCall:
         a.v_stride, a.o_stride = _strides3(v, "v"), _strides3(o, "o")
         keep = [q, k, v, o]
         _set_rope_extra(a, keep, rope_precision, rope_mscale, rope_factors)
+        for name, w in (("q_norm_w", q_norm_weight), ("k_norm_w", k_norm_weight)):
+            if w is not None:
+                if w.dtype != q.dtype or w.dim() != 1 or w.shape[0] != D or not w.is_contiguous():
+                    raise MzattnError(MZ_ERR_SHAPE, f"{name} must be a contiguous [head_dim] tensor of q's dtype")
+                setattr(a, name, w.data_ptr())
+                keep.append(w)
+        a.norm_eps = float(norm_eps)
         if (mask is not None) + (seg_q is not None) + bool(causal) > 1:
             raise MzattnError(MZ_ERR_UNSUPPORTED, "give at most one of mask, segment ids, causal")
         if causal:
@@ -428,7 +439,7 @@ class FwdCall:
 def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
-               rope_factors=None, out=None, return_lse: bool = False, workspace=None, stream=None):
+               rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6, out=None, return_lse: bool = False, workspace=None, stream=None):
     """Masked bidirectional attention forward (see ``mzattn_fwd`` in
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
     same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
@@ -436,7 +447,8 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = Fal
     Returns o (and lse when ``return_lse``)."""
     return FwdCall(q, k, v, mask=mask, seg_q=seg_q, seg_k=seg_k, causal=causal, pos_q=pos_q, pos_k=pos_k,
                    scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, rope_precision=rope_precision,
-                   rope_mscale=rope_mscale, rope_factors=rope_factors, out=out,
+                   rope_mscale=rope_mscale, rope_factors=rope_factors, q_norm_weight=q_norm_weight,
+                   k_norm_weight=k_norm_weight, norm_eps=norm_eps, out=out,
                    return_lse=return_lse, workspace=workspace, stream=stream)()
 
 

@@ -64,7 +64,7 @@ mz::RopeSpec rope_spec(double base, int32_t precision, float mscale, const float
 struct FwdPlan {
   bool empty = false;
   int n_qt = 0, n_kt = 0, bm = 0;
-  int n_rot = 0, n_rot_kv = 0, tab_len = 0;
+  int n_rot = 0, n_rot_kv = 0, n_rotk = 0, tab_len = 0;
   int Bm = 1, Hm = 1;
   size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_kpos = 0, off_cls = 0;
   size_t off_bits = 0;
@@ -120,7 +120,13 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
   if (G > 1 && n_rot != 0 && n_rot != Hq)
     return fail(MZ_ERR_UNSUPPORTED, "pe_attn_head %d with GQA (G = %d): only 0 or all heads", a->pe_attn_head, G);
   pl->n_rot = n_rot;
-  pl->n_rot_kv = G > 1 ? (n_rot ? Hkv : 0) : n_rot;
+  pl->n_rotk = G > 1 ? (n_rot ? Hkv : 0) : n_rot;
+  // K heads that pass through the workspace: the rotated ones, or all when
+  // k is normalised
+  pl->n_rot_kv = a->k_norm_w != nullptr ? Hkv : pl->n_rotk;
+  if (!isfinite(a->norm_eps) || a->norm_eps < 0.f) return fail(MZ_ERR_VALUE, "norm_eps must be finite and >= 0");
+  if ((a->q_norm_w && !aligned(a->q_norm_w, 16)) || (a->k_norm_w && !aligned(a->k_norm_w, 16)))
+    return fail(MZ_ERR_ALIGN, "q_norm_w / k_norm_w must be 16-byte aligned");
 
   pl->bm = a->dtype == MZ_F32 ? mz::F32_BM : mz::FWD_BM;
   pl->n_qt = (a->seq_q + pl->bm - 1) / pl->bm;
@@ -320,7 +326,9 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
     p.qs[i] = a->q_stride[i]; p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; p.os[i] = a->o_stride[i];
   }
   char* ws = static_cast<char*>(a->workspace);
-  p.n_rot = pl.n_rot; p.n_rot_kv = pl.n_rot_kv;
+  p.n_rot = pl.n_rot; p.n_rot_kv = pl.n_rot_kv; p.n_rotk = pl.n_rotk;
+  p.q_norm_w = a->q_norm_w; p.k_norm_w = a->k_norm_w; p.norm_eps = a->norm_eps;
+  if (pl.n_rot_kv > 0) p.k_rot = ws + pl.off_krot;
   p.rope_style = a->rope_style;
   if (pl.n_rot > 0) {
     p.rs = rope_spec(a->rope_base, a->rope_precision, a->rope_mscale, a->rope_factors);
@@ -334,7 +342,6 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
     else if (a->mask_kind == MZ_MASK_SEGMENT) {
       p.pos_k_mode = mz::POS_SEGMENT; p.pos_k = reinterpret_cast<int32_t*>(ws + pl.off_kpos); p.pos_k_sb = a->seq_k;
     } else p.pos_k_mode = mz::POS_ARANGE;
-    if (pl.n_rot_kv > 0) p.k_rot = ws + pl.off_krot;
   }
   p.Bm = pl.Bm; p.Hm = pl.Hm;
   if (a->mask_kind == MZ_MASK_BOOL) {

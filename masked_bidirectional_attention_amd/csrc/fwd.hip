@@ -171,13 +171,16 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
 
 // One thread per 8 consecutive elements of a K row: 4 adjacent pairs
 // (interleaved), or with HALF 8 elements of the first half and their 8
-// partners D/2 further (half split).
+// partners D/2 further (half split).  The q8 threads of a row are adjacent
+// lanes, so the row's sum of squares (RMSNorm of k) is a reduction over
+// them.  Heads below n_rotk are rotated; all are normalised when k_norm_w
+// is set.
 template <typename T, bool HALF>
 __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int q8 = HALF ? p.D / 16 : p.D / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-  if (idx >= nrows * q8) return;
+  if (idx >= nrows * q8) return;  // whole rows only (q8 divides the block)
   const int64_t row = idx / q8;
   const int d0 = (int)(idx % q8) * 8;
   const int j = (int)(row % p.Sk);
@@ -185,50 +188,86 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
   const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + d0;
   uint16_t* dst = (uint16_t*)p.k_rot + row * p.D + d0;
-  const int pos = key_position(p, b, j);
-  if constexpr (!HALF) {
-    *(uint4*)dst = rope_quad<T>(*(const uint4*)src, p.rope_tab, p.rope_tab_len, pos, d0, p.D, p.rs);
-  } else {
-    const int hd = p.D / 2;
-    const uint4 x0 = *(const uint4*)src, x1 = *(const uint4*)(src + hd);
-    uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+  const bool rot = hk < p.n_rotk;
+  const int hd = p.D / 2;
+  constexpr int NE = HALF ? 16 : 8;
+  float x[NE];  // HALF: x[0..7] at d0 + e, x[8..15] at d0 + hd + e
+  {
+    const uint4 a0 = *(const uint4*)src;
+    const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float r[2][2];
+    for (int e = 0; e < 8; ++e) x[e] = Elem<T>::to_f32((uint16_t)(w0[e / 2] >> (16 * (e & 1))));
+    if constexpr (HALF) {
+      const uint4 a1 = *(const uint4*)(src + hd);
+      const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
-        const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
-        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, d0 + 2 * t + e, p.D, p.rs);
-        r[0][e] = fmaf(a, cs.x, -c * cs.y);
-        r[1][e] = fmaf(c, cs.x, a * cs.y);
-      }
-      lo[t] = Elem<T>::pack2(r[0][0], r[0][1]);
-      hi[t] = Elem<T>::pack2(r[1][0], r[1][1]);
+      for (int e = 0; e < 8; ++e) x[8 + e] = Elem<T>::to_f32((uint16_t)(w1[e / 2] >> (16 * (e & 1))));
     }
-    *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    *(uint4*)(dst + hd) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+  if (p.k_norm_w != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) ss = fmaf(x[e], x[e], ss);
+    for (int off = q8 / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = rsqrtf(ss / (float)p.D + p.norm_eps);
+    const uint16_t* wp = (const uint16_t*)p.k_norm_w;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x[e] = x[e] * inv * Elem<T>::to_f32(wp[(e < 8 ? d0 : d0 + hd) + (e & 7)]);
+  }
+  if (rot) {
+    const int pos = key_position(p, b, j);
+#pragma unroll
+    for (int t = 0; t < (HALF ? 8 : 4); ++t) {
+      // pair: interleaved (x[2t], x[2t+1]) of pair index d0/2 + t; half
+      // split (x[t], x[8+t]) of pair index d0 + t
+      const int ia = HALF ? t : 2 * t, ic = HALF ? 8 + t : 2 * t + 1;
+      const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, HALF ? d0 + t : d0 / 2 + t, p.D, p.rs);
+      const float a = x[ia], c = x[ic];
+      x[ia] = fmaf(a, cs.x, -c * cs.y);
+      x[ic] = fmaf(c, cs.x, a * cs.y);
+    }
+  }
+  uint32_t o0[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o0[t] = Elem<T>::pack2(x[2 * t], x[2 * t + 1]);
+  *(uint4*)dst = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  if constexpr (HALF) {
+    uint32_t o1[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o1[t] = Elem<T>::pack2(x[8 + 2 * t], x[8 + 2 * t + 1]);
+    *(uint4*)(dst + hd) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
   }
 }
 
+// fp32: one thread per pair; the D/2 threads of a row are adjacent lanes.
 __global__ void k_rotate32_kernel(const FwdParams p) {
   const int half = p.D / 2;
   const int rows_per_blk = blockDim.x / half;
   const int64_t row = (int64_t)blockIdx.x * rows_per_blk + threadIdx.x / half;
   const int i = threadIdx.x % half;
   const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-  if (row >= nrows) return;
+  if (row >= nrows) return;  // whole rows only
   const int j = (int)(row % p.Sk);
   const int hk = (int)((row / p.Sk) % p.n_rot_kv);
   const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
   // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
   const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
   const float* src = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2];
-  const float2 x = make_float2(src[d0], src[d1]);
-  const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.rs);
+  float2 x = make_float2(src[d0], src[d1]);
+  if (p.k_norm_w != nullptr) {
+    float ss = fmaf(x.x, x.x, x.y * x.y);
+    for (int off = half / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = rsqrtf(ss / (float)p.D + p.norm_eps);
+    const float* wp = (const float*)p.k_norm_w;
+    x = make_float2(x.x * inv * wp[d0], x.y * inv * wp[d1]);
+  }
+  if (hk < p.n_rotk) {
+    const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.rs);
+    x = make_float2(fmaf(x.x, cs.x, -x.y * cs.y), fmaf(x.y, cs.x, x.x * cs.y));
+  }
   float* dst = (float*)p.k_rot + row * p.D;
-  dst[d0] = fmaf(x.x, cs.x, -x.y * cs.y);
-  dst[d1] = fmaf(x.y, cs.x, x.x * cs.y);
+  dst[d0] = x.x;
+  dst[d1] = x.y;
 }
 
 // ---------------------------------------------------------------------------
@@ -368,6 +407,31 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     const float sc = p.scale_log2;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = qvalid ? *(const uint4*)(qrow + s * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+    // RMSNorm of q: this lane holds half of the row (elements s*16 + hh*8
+    // + e), lane ^ 32 the other half
+    const bool qnorm = p.q_norm_w != nullptr;
+    float qinv = 1.f;
+    uint4 wq[NS];
+    if (qnorm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        wq[s] = *(const uint4*)((const uint16_t*)p.q_norm_w + s * 16 + hh * 8);
+        const uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float a = Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), c = Elem<T>::to_f32((uint16_t)(wv[t] >> 16));
+          ss = fmaf(a, a, fmaf(c, c, ss));
+        }
+      }
+      qinv = rsqrtf(half_swap_sum(ss) / (float)D + p.norm_eps);
+    }
+    // element e (0..7) of piece s, normalised when q_norm_w is set
+    auto qn = [&](float x, int s, int e) -> float {
+      if (!qnorm) return x;
+      const uint32_t w2 = e < 4 ? (e < 2 ? wq[s].x : wq[s].y) : (e < 6 ? wq[s].z : wq[s].w);
+      return x * qinv * Elem<T>::to_f32((uint16_t)(w2 >> (16 * (e & 1))));
+    };
     if (qvalid && rot && p.rope_style == 1) {
       // half split: element e of chunk s pairs with element e of chunk
       // s + NS/2 (d and d + D/2), both held by this lane
@@ -380,8 +444,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           float r[2][2];  // [first half, second half][element 2t, 2t + 1]
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float a = Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e)));
-            const float c = Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e)));
+            const float a = qn(Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e))), s, 2 * t + e);
+            const float c = qn(Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e))), s + NS / 2, 2 * t + e);
             const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8 + 2 * t + e, D, p.rs);
             r[0][e] = fmaf(a, cs.x, -c * cs.y);
             r[1][e] = fmaf(c, cs.x, a * cs.y);
@@ -400,8 +464,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         const int d0 = s * 16 + hh * 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          float a = Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF));
-          float c = Elem<T>::to_f32((uint16_t)(wv[t] >> 16));
+          float a = qn(Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), s, 2 * t);
+          float c = qn(Elem<T>::to_f32((uint16_t)(wv[t] >> 16)), s, 2 * t + 1);
           if (rot) {
             const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, d0 / 2 + t, D, p.rs);
             const float ra = fmaf(a, cs.x, -c * cs.y);
@@ -937,9 +1001,18 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
     const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
     // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
     const bool half = p.rope_style == 1;
+    // RMSNorm of q (one lane holds the whole row)
+    float qinv = 1.f;
+    const float* wq = (const float*)p.q_norm_w;
+    if (wq != nullptr && qvalid) {
+      float ss = 0.f;
+      for (int d = 0; d < D; ++d) ss = fmaf(qrow[d], qrow[d], ss);
+      qinv = rsqrtf(ss / (float)D + p.norm_eps);
+    }
     for (int i = 0; i < D / 2; ++i) {
       const int d0 = half ? i : 2 * i, d1 = half ? i + D / 2 : 2 * i + 1;
       float2 x = qvalid ? make_float2(qrow[d0], qrow[d1]) : make_float2(0.f, 0.f);
+      if (wq != nullptr) x = make_float2(x.x * qinv * wq[d0], x.y * qinv * wq[d1]);
       if (rot && qvalid) {
         const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, i, D, p.rs);
         const float a = fmaf(x.x, cs.x, -x.y * cs.y);

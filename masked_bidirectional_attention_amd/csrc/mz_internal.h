@@ -38,8 +38,13 @@ struct FwdParams {
   const void* v;
   void* o;
   int64_t qs[3], ks[3], vs[3], os[3];
-  // rotary embedding
-  int n_rot, n_rot_kv;
+  // rotary embedding; the K pass covers heads [0, n_rot_kv) (rotated when
+  // below n_rotk, normalised when k_norm_w is set)
+  int n_rot, n_rot_kv, n_rotk;
+  // q / k RMSNorm weights [D] (storage dtype) or nullptr
+  const void* q_norm_w;
+  const void* k_norm_w;
+  float norm_eps;
   int rope_style;  // 0 interleaved (2i, 2i+1), 1 half split (i, i + D/2)
   RopeSpec rs;
   int pos_q_mode, pos_k_mode;

@@ -12,6 +12,7 @@ from .mzref import (  # noqa: F401
     live_set_fwd,
     mzref_decode,
     mzref_decode_append,
+    rms_norm,
     rope_cos_sin,
     round_bf16,
     mzref_fwd,

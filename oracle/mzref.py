@@ -200,6 +200,14 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float, style: str = "interleaved"
     raise ValueError(style)
 
 
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * w over the last axis (the q / k
+    normalisation of the Qwen3 LM, OmniVoice page, 'What matches upstream':
+    q and k are normalised separately, as transformers does, before RoPE)."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
 def segment_positions(seg: np.ndarray) -> np.ndarray:
     """Positions that restart at 0 at the start of every run of equal ids
     (OmniVoice page, 'Memory and speed': each packed block has its own
@@ -283,7 +291,8 @@ def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
               rope_base: float = 0.0, pe_attn_head: int = -1,
               pos_q=None, pos_k=None, mask_kind: str = "none", mask=None,
               seg_q=None, seg_k=None, heads=None, rope_style: str = "interleaved",
-              rope_precision: str = "exact", rope_factors=None, rope_mscale: float = 1.0):
+              rope_precision: str = "exact", rope_factors=None, rope_mscale: float = 1.0,
+              q_norm_w=None, k_norm_w=None, norm_eps: float = 1e-6):
     """Oracle of the bidirectional forward.
 
     q_bits [B, Hq, Sq, D], k_bits / v_bits [B, Hkv, Sk, D] (storage bits
@@ -331,6 +340,10 @@ def mzref_fwd(dtype: str, q_bits, k_bits, v_bits, *, scale: float = 0.0,
                 continue
             hk = h // G
             qh, kh, vh = q[b, h], k[b, hk], v[b, hk]
+            if q_norm_w is not None:
+                qh = rms_norm(qh, decode(q_norm_w, dtype), norm_eps)
+            if k_norm_w is not None:
+                kh = rms_norm(kh, decode(k_norm_w, dtype), norm_eps)
             if h < n_rot:
                 qh = rope(qh, pq[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)
                 kh = rope(kh, pk[b], rope_base, rope_style, rope_precision, rope_factors, rope_mscale)

@@ -598,6 +598,30 @@ def pin_rope_bf16_table_vs_torch():
     assert np.array_equal(mzref.round_bf16(c_ref), c_ref)
 
 
+def pin_qk_rms_norm():
+    """q / k RMSNorm before RoPE: the forward with norm weights equals SDPA
+    over q and k normalised by torch's rms_norm (library routine) and then
+    rotated (complex form)."""
+    rng = np.random.default_rng(51)
+    B, Hq, Hkv, S, D = 1, 4, 2, 20, 16
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)   # inputs exact in fp32
+    q, k, v = f32(_rand(rng, B, Hq, S, D) * 3.0), f32(_rand(rng, B, Hkv, S, D) * 0.2), _rand(rng, B, Hkv, S, D)
+    wq, wk = _rand(rng, D), _rand(rng, D)
+    o, _ = mzref.mzref_fwd("f32", _bits64(q), _bits64(k), _bits64(v), rope_base=1e4, q_norm_w=_bits64(wq),
+                           k_norm_w=_bits64(wk), norm_eps=1e-6)
+    qn = F.rms_norm(torch.from_numpy(q), (D,), torch.from_numpy(wq), eps=1e-6).numpy()
+    kn = F.rms_norm(torch.from_numpy(k), (D,), torch.from_numpy(wk), eps=1e-6).numpy()
+    pos = np.arange(S)
+    ref = _sdpa(_rope_complex(qn, pos, 1e4), _rope_complex(kn, pos, 1e4), v, gqa=True)
+    _close(o, ref, 1e-12, "q/k rms norm")
+    # the scale of q or k then does not matter
+    o2, _ = mzref.mzref_fwd("f32", _bits64(q * 4.0), _bits64(k * 0.25), _bits64(v), rope_base=1e4,
+                            q_norm_w=_bits64(wq), k_norm_w=_bits64(wk), norm_eps=0.0)
+    o3, _ = mzref.mzref_fwd("f32", _bits64(q), _bits64(k), _bits64(v), rope_base=1e4,
+                            q_norm_w=_bits64(wq), k_norm_w=_bits64(wk), norm_eps=0.0)
+    _close(o2, o3, 1e-12, "rms norm scale invariance")
+
+
 ALL_PINS = [
     pin_fp16_decode, pin_bf16_decode, pin_fp32_decode,
     pin_rope_complex_form, pin_rope_hand_values, pin_rope_properties,
@@ -610,4 +634,5 @@ ALL_PINS = [
     pin_append_empty_cache_is_causal_sdpa, pin_append_single_token_first_row,
     pin_append_equals_sdpa_on_updated_cache, pin_append_overflow,
     pin_longrope_vs_transformers, pin_rope_fp16_angles_vs_torch, pin_rope_bf16_table_vs_torch,
+    pin_qk_rms_norm,
 ]

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.mzattn_version() == 300
+    assert lib.mzattn_version() == 400
     for code in range(0, -11, -1):
         msg = lib.mzattn_strerror(code).decode()
         assert msg and msg != "unknown status", code
@@ -437,3 +437,30 @@ def test_rope_options_valid(lib):
         a = good_fwd()
         a.rope_precision, a.rope_mscale, a.rope_factors = prec, 1.118, FAKE + 0x6000000
         assert vfwd(lib, a) == 0, lib.mzattn_last_error()
+
+
+def test_norm_options_checked(lib):
+    a = good_fwd()
+    a.q_norm_w, a.k_norm_w, a.norm_eps = FAKE + 0x7000000, FAKE + 0x7001000, 1e-6
+    with_workspace(lib, a)
+    assert vfwd(lib, a) == 0, lib.mzattn_last_error()
+    a.k_norm_w = FAKE + 0x7001000 + 8
+    assert vfwd(lib, a) == B.MZ_ERR_ALIGN
+    a.k_norm_w = None
+    a.norm_eps = -1.0
+    assert vfwd(lib, a) == B.MZ_ERR_VALUE
+    a.norm_eps = float("inf")
+    assert vfwd(lib, a) == B.MZ_ERR_VALUE
+
+
+def test_k_norm_needs_the_k_pass_workspace(lib):
+    """With k normalised every K head passes through the workspace, RoPE or
+    not, so the workspace grows."""
+    a = good_fwd()
+    a.rope_base = 0.0
+    need0 = ctypes.c_size_t(0)
+    assert lib.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need0)) == 0
+    a.k_norm_w = FAKE + 0x7000000
+    need1 = ctypes.c_size_t(0)
+    assert lib.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need1)) == 0
+    assert need1.value >= need0.value + a.batch * a.heads_kv * a.seq_k * a.head_dim * 2

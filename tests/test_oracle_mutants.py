@@ -64,6 +64,10 @@ MUTANTS = {
     "fp16_angle_unrounded": ("a16 = (p16 * th16).astype(np.float16).astype(np.float64)", "a16 = p16 * th16"),
     "bf16_rounding_truncates": ("r = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))",
                                 "r = (b >> np.uint64(16))"),
+    "rms_norm_sum_not_mean": ("ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.sum(x * x, axis=-1, keepdims=True)"),
+    "rms_norm_eps_outside": ("return x / np.sqrt(ms + eps) * w", "return x / (np.sqrt(ms) + eps) * w"),
+    "k_norm_uses_q_weight": ("kh = rms_norm(kh, decode(k_norm_w, dtype), norm_eps)",
+                             "kh = rms_norm(kh, decode(q_norm_w, dtype), norm_eps)"),
     "causal_transposed": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                           "live = np.arange(Sk)[None, :] >= np.arange(Sq)[:, None]"),
 }

@@ -630,3 +630,52 @@ def test_rope_variants_decode_and_append(variant):
                                                 W.to_bits(vc), [2000, 2997], rope_base=1e4, rope_precision=prec,
                                                 rope_factors=fo, rope_mscale=ms)
     assert_parity("bf16", oa, refa, f"append rope {variant}")
+
+
+# --------------------------------------------------------------------------
+# q / k RMSNorm before RoPE (forward)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [
+    # dtype, D, mask kind, rope_base, pe_attn_head, style, which norms
+    ("bf16", 128, W.MASK_SEGMENT, 1e6, -1, "interleaved", "qk"),
+    ("bf16", 128, W.MASK_BOOL, 1e6, -1, "half", "qk"),
+    ("f16", 64, W.MASK_BOOL, 1e4, 1, "interleaved", "qk"),    # RoPE on head 0 only, norm on all
+    ("bf16", 128, W.MASK_NONE, 0.0, -1, "interleaved", "k"),   # no RoPE: the K pass only normalises
+    ("f16", 128, W.MASK_CAUSAL, 1e4, -1, "half", "q"),
+    ("f32", 64, W.MASK_BOOL, 1e4, -1, "interleaved", "qk"),
+    ("f32", 128, W.MASK_NONE, 0.0, -1, "half", "q"),
+], ids=lambda c: "-".join(map(str, c)))
+def test_qk_rms_norm(cfg):
+    import masked_bidirectional_attention_amd as mz
+    dtype, D, kind, base, pe, style, which = cfg
+    Hq, Hkv = (4, 4) if pe >= 0 else (8, 2)
+    case = W.random_fwd(zlib.crc32(repr(cfg).encode()) % 10000, 2, Hq, Hkv, 200, 200, D, dtype, kind,
+                        rope_base=base, pe_attn_head=pe, mask_shape="key", n_segments=2)
+    cast = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    gen = torch.Generator().manual_seed(11)
+    wq = (1.0 + 0.5 * torch.randn(D, generator=gen)).to(cast) if "q" in which else None
+    wk = (1.0 + 0.5 * torch.randn(D, generator=gen)).to(cast) if "k" in which else None
+    # the normalised inputs far from unit scale, so a missing normalisation
+    # shows (the others keep N(0,1) logits: a 4x q would make the softmax
+    # sharper than the 16-bit tolerances are stated for)
+    q = (case.q.float() * (4.0 if wq is not None else 1.0)).to(cast)
+    k = (case.k.float() * (0.3 if wk is not None else 1.0)).to(cast)
+    kw = dict(rope_base=base, pe_attn_head=pe, rope_style=style, q_norm_weight=dev(wq), k_norm_weight=dev(wk),
+              norm_eps=1e-6)
+    if kind == W.MASK_BOOL:
+        kw["mask"] = dev(case.mask)
+    elif kind == W.MASK_SEGMENT:
+        kw["seg_q"], kw["seg_k"] = dev(case.seg_q), dev(case.seg_k)
+    elif kind == W.MASK_CAUSAL:
+        kw["causal"] = True
+    o = mz.mzattn_fwd(dev(q), dev(k), dev(case.v), **kw)
+    torch.cuda.synchronize()
+    ref, _ = mzref.mzref_fwd(dtype, W.to_bits(q), W.to_bits(k), W.to_bits(case.v), rope_base=base,
+                             pe_attn_head=pe, rope_style=style, mask_kind=case.mask_kind,
+                             mask=None if case.mask is None else case.mask.numpy(),
+                             seg_q=None if case.seg_q is None else case.seg_q.numpy(),
+                             seg_k=None if case.seg_k is None else case.seg_k.numpy(),
+                             q_norm_w=None if wq is None else W.to_bits(wq),
+                             k_norm_w=None if wk is None else W.to_bits(wk), norm_eps=1e-6)
+    assert_parity(dtype, o, ref, f"rms norm {cfg}")
