@@ -321,6 +321,25 @@ def main(argv=None):
               "TFLOP/s": round(cp_gflop / cp_us * 1e3, 1),
               "frac": round(cp_gflop / cp_us * 1e3 / PEAK_BF16_TFLOPS, 4)}
 
+    # ---- the packed workload with q / k RMSNorm before RoPE (reported, not
+    # the headline): execute = K pass (normalise + rotate) + attention kernel
+    gen_n = torch.Generator().manual_seed(3)
+    wq = (1.0 + 0.1 * torch.randn(128, generator=gen_n)).to(torch.bfloat16).to(dev)
+    wk = (1.0 + 0.1 * torch.randn(128, generator=gen_n)).to(torch.bfloat16).to(dev)
+    fn = mz.FwdCall(fq, fk, fv, seg_q=seg, seg_k=seg, rope_base=c3.rope_base, q_norm_weight=wq, k_norm_weight=wk)
+    fn.plan()
+    for _ in range(5):
+        fn.execute()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(50):
+        fn.execute()
+    e1.record()
+    torch.cuda.synchronize()
+    norm_us = e0.elapsed_time(e1) / 50 * 1e3
+    qk_norm = {"workload": "packed-guidance workload with q / k RMSNorm before RoPE", "execute_us": round(norm_us, 2),
+               "TFLOP/s": round(fwd_flops() / (norm_us * 1e-6) / 1e12, 1)}
+
     # ---- the append step (reported, not the headline): the static-cache
     # step that reads the filled length on the device, rotates q and the new
     # key, writes the new K/V rows into the cache and attends keys
@@ -433,6 +452,7 @@ def main(argv=None):
             "by_fill": by_fill,
         },
         "causal_prefill": causal,
+        "qk_norm": qk_norm,
         "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
                                       "length on the device, RoPE base 1e4 on q and the new key",
                           "by_fill": append},
