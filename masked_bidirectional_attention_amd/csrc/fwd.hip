@@ -398,25 +398,53 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   const int qi = qt * BM + wave * 32 + l32;
   const bool qvalid = qi < p.Sq;
 
-  // ---- Q fragment, pre-scaled: B operand of S^T = K Q^T
+  // ---- Q fragment, pre-scaled: B operand of S^T = K Q^T.  Its loads (q,
+  // the norm weights, the cos / sin table entries) are issued here; the
+  // arithmetic (finish_q) runs once the first K / V tile copies are
+  // issued, so the two latencies overlap.
   uint4 qf[NS];
-  {
-    const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
-    const bool rot = h < p.n_rot;
-    const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
-    const float sc = p.scale_log2;
+  const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
+  const bool rot = h < p.n_rot;
+  const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
+  const float qsc = p.scale_log2;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = qvalid ? *(const uint4*)(qrow + s * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
-    // RMSNorm of q: this lane holds half of the row (elements s*16 + hh*8
-    // + e), lane ^ 32 the other half
-    const bool qnorm = p.q_norm_w != nullptr;
+  for (int s = 0; s < NS; ++s) qf[s] = qvalid ? *(const uint4*)(qrow + s * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+  // RMSNorm of q: this lane holds half of the row (elements s*16 + hh*8
+  // + e), lane ^ 32 the other half
+  const bool qnorm = p.q_norm_w != nullptr;
+  uint4 wq[NS];
+  if (qnorm) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wq[s] = *(const uint4*)((const uint16_t*)p.q_norm_w + s * 16 + hh * 8);
+  }
+  // cos / sin of this lane's pairs at the query's position, read from the
+  // table as 16-byte vectors, all issued before any is used: interleaved,
+  // piece s holds pairs s*8 + hh*4 + t (t < 4), slot 4s + t; half split,
+  // piece s < NS/2 holds pairs s*16 + hh*8 + j (j < 8), slot 8s + j; slot
+  // m is half of tb[m / 2].  A position past the table (rare) takes the
+  // direct formula instead (same bits), a branch at the use.
+  const bool in_tab = qpos >= 0 && qpos < p.rope_tab_len;
+  float4 tb[2 * NS];
+  if (qvalid && rot) {
+    const float2* trow = p.rope_tab + (size_t)(in_tab ? qpos : 0) * (D / 2);
+    if (p.rope_style == 1) {
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tb[4 * s + j] = ((const float4*)(trow + s * 16 + hh * 8))[j];
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) tb[2 * s + j] = ((const float4*)(trow + s * 8 + hh * 4))[j];
+    }
+  }
+  auto finish_q = [&]() {
     float qinv = 1.f;
-    uint4 wq[NS];
     if (qnorm) {
       float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        wq[s] = *(const uint4*)((const uint16_t*)p.q_norm_w + s * 16 + hh * 8);
         const uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -427,10 +455,16 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       qinv = rsqrtf(half_swap_sum(ss) / (float)D + p.norm_eps);
     }
     // element e (0..7) of piece s, normalised when q_norm_w is set
-    auto qn = [&](float x, int s, int e) -> float {
+    auto qn = [&](float x, int s, int e) __attribute__((always_inline)) -> float {
       if (!qnorm) return x;
       const uint32_t w2 = e < 4 ? (e < 2 ? wq[s].x : wq[s].y) : (e < 6 ? wq[s].z : wq[s].w);
       return x * qinv * Elem<T>::to_f32((uint16_t)(w2 >> (16 * (e & 1))));
+    };
+    auto cs_at = [&](int m, int pair) -> float2 {
+      const float4 v = tb[m >> 1];
+      float2 cs = (m & 1) ? make_float2(v.z, v.w) : make_float2(v.x, v.y);
+      if (__builtin_expect(!in_tab, 0)) cs = rope_cs_direct(qpos, pair, D, p.rs);
+      return cs;
     };
     if (qvalid && rot && p.rope_style == 1) {
       // half split: element e of chunk s pairs with element e of chunk
@@ -446,12 +480,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           for (int e = 0; e < 2; ++e) {
             const float a = qn(Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e))), s, 2 * t + e);
             const float c = qn(Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e))), s + NS / 2, 2 * t + e);
-            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, s * 16 + hh * 8 + 2 * t + e, D, p.rs);
+            const float2 cs = cs_at(8 * s + 2 * t + e, s * 16 + hh * 8 + 2 * t + e);
             r[0][e] = fmaf(a, cs.x, -c * cs.y);
             r[1][e] = fmaf(c, cs.x, a * cs.y);
           }
-          lo[t] = Elem<T>::pack2(r[0][0] * sc, r[0][1] * sc);
-          hi[t] = Elem<T>::pack2(r[1][0] * sc, r[1][1] * sc);
+          lo[t] = Elem<T>::pack2(r[0][0] * qsc, r[0][1] * qsc);
+          hi[t] = Elem<T>::pack2(r[1][0] * qsc, r[1][1] * qsc);
         }
         qf[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         qf[s + NS / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -467,18 +501,18 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           float a = qn(Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), s, 2 * t);
           float c = qn(Elem<T>::to_f32((uint16_t)(wv[t] >> 16)), s, 2 * t + 1);
           if (rot) {
-            const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, d0 / 2 + t, D, p.rs);
+            const float2 cs = cs_at(4 * s + t, d0 / 2 + t);
             const float ra = fmaf(a, cs.x, -c * cs.y);
             const float rc = fmaf(c, cs.x, a * cs.y);
             a = ra;
             c = rc;
           }
-          wv[t] = Elem<T>::pack2(a * sc, c * sc);
+          wv[t] = Elem<T>::pack2(a * qsc, c * qsc);
         }
         qf[s] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
     }
-  }
+  };
 
   // ---- K / V sources
   const uint16_t* kbase;
@@ -608,11 +642,6 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     }
   };
 
-  // every prologue load completes here, so that no wait for it is left
-  // inside the tile loop (where it would also wait for the tile copies)
-#pragma unroll
-  for (int s = 0; s < NS; ++s) __asm__ volatile("" ::"v"(qf[s].x), "v"(qf[s].y), "v"(qf[s].z), "v"(qf[s].w));
-  __asm__ volatile("" ::"v"(lo), "v"(hi));
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[ND];
@@ -824,6 +853,13 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     load_v(kt, 0);
   }
   if (kn < kt_end) load_k(kn, 1);
+  finish_q();
+  // every prologue load completes here (the first tile copies are in flight
+  // meanwhile), so that no wait for one is left inside the tile loop, where
+  // it would also wait for the tile copies
+#pragma unroll
+  for (int s = 0; s < NS; ++s) __asm__ volatile("" ::"v"(qf[s].x), "v"(qf[s].y), "v"(qf[s].z), "v"(qf[s].w));
+  __asm__ volatile("" ::"v"(lo), "v"(hi));
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   auto rescale_step = [&](f32x16_t (&sc)[2]) {
@@ -1182,17 +1218,22 @@ static void launch_mfma(const FwdParams& p, unsigned nwork, int nstr, hipStream_
 }
 
 // Key streams per work-group.  Two when there are no more work-groups than
-// CUs: each CU then holds one query tile, the one-stream kernel would run a
-// single wave per SIMD, and splitting the keys of the tile over two waves
-// per SIMD shortens the chain of steps (measured 7-13 % faster for 128 and
-// 256 work-groups at 2048 keys).  With more work-groups the one-stream
-// kernel already places two per CU and is faster.  MZATTN_KEY_STREAMS=1|2
-// overrides the choice.
-static int key_streams(unsigned nwork) {
+// CUs and the rows are long: each CU then holds one query tile, the
+// one-stream kernel would run a single wave per SIMD, and splitting the keys
+// of the tile over two waves per SIMD shortens the chain of steps (measured
+// 7-13 % faster for 128 and 256 work-groups at 2048 keys, 32 key tiles).
+// With 16 key tiles or fewer per row the second stream's own prologue and
+// the final merge cost more than the shorter chain saves (measured slower
+// at 16 to 1024 keys), and with more work-groups than CUs the one-stream
+// kernel already places two per CU.  MZATTN_KEY_STREAMS=1|2 overrides the
+// choice.
+constexpr int KEY_STREAMS_MIN_TILES = 24;
+static int key_streams(unsigned nwork, int n_kt) {
   if (const char* e = getenv("MZATTN_KEY_STREAMS")) {
     if (e[0] == '1' && e[1] == 0) return 1;
     if (e[0] == '2' && e[1] == 0) return 2;
   }
+  if (n_kt < KEY_STREAMS_MIN_TILES) return 1;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     ncu = 256;
@@ -1206,9 +1247,9 @@ hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
     if (p.D == 64) fwd_f32_kernel<64><<<dim3(nwork), dim3(64), 0, s>>>(p);
     else fwd_f32_kernel<128><<<dim3(nwork), dim3(64), 0, s>>>(p);
   } else if (p.dtype == 2) {
-    launch_mfma<BF16>(p, nwork, key_streams(nwork), s);
+    launch_mfma<BF16>(p, nwork, key_streams(nwork, p.n_kt), s);
   } else {
-    launch_mfma<F16>(p, nwork, key_streams(nwork), s);
+    launch_mfma<F16>(p, nwork, key_streams(nwork, p.n_kt), s);
   }
   return hipGetLastError();
 }
