@@ -340,6 +340,28 @@ def main(argv=None):
     qk_norm = {"workload": "packed-guidance workload with q / k RMSNorm before RoPE", "execute_us": round(norm_us, 2),
                "TFLOP/s": round(fwd_flops() / (norm_us * 1e-6) / 1e12, 1)}
 
+    # ---- short bidirectional sequences (reported, not the headline): the
+    # latency of one forward execute (K rotation + attention) for a CFG
+    # pair, Hq 16 / Hkv 2, D 128, bf16, RoPE, no mask, the shape class of a
+    # local DiT / encoder step run many times per generated patch
+    short = []
+    for S in (16, 64, 128, 256):
+        gs_ = torch.Generator().manual_seed(S)
+        sq = torch.randn(2, 16, S, 128, generator=gs_).to(torch.bfloat16).to(dev)
+        sk = torch.randn(2, 2, S, 128, generator=gs_).to(torch.bfloat16).to(dev)
+        sv = torch.randn(2, 2, S, 128, generator=gs_).to(torch.bfloat16).to(dev)
+        sc_ = mz.FwdCall(sq, sk, sv, rope_base=1e4)
+        sc_.plan()
+        for _ in range(10):
+            sc_.execute()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(100):
+            sc_.execute()
+        e1.record()
+        torch.cuda.synchronize()
+        short.append({"seq": S, "execute_us": round(e0.elapsed_time(e1) / 100 * 1e3, 2)})
+
     # ---- the append step (reported, not the headline): the static-cache
     # step that reads the filled length on the device, rotates q and the new
     # key, writes the new K/V rows into the cache and attends keys
@@ -453,6 +475,8 @@ def main(argv=None):
         },
         "causal_prefill": causal,
         "qk_norm": qk_norm,
+        "short_bidirectional": {"workload": "B 2 (CFG), Hq 16 / Hkv 2, D 128, bf16, RoPE base 1e4, no mask",
+                                "by_seq": short},
         "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
                                       "length on the device, RoPE base 1e4 on q and the new key",
                           "by_fill": append},
