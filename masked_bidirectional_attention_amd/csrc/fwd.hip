@@ -174,54 +174,74 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
 // partners D/2 further (half split).  The q8 threads of a row are adjacent
 // lanes, so the row's sum of squares (RMSNorm of k) is a reduction over
 // them.  Heads below n_rotk are rotated; all are normalised when k_norm_w
-// is set.
+// is set.  Grid: x over the Sk * q8 threads of one (batch, head) (32-bit
+// index math), y the K head, z the batch row.
 template <typename T, bool HALF>
 __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int q8 = HALF ? p.D / 16 : p.D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-  if (idx >= nrows * q8) return;  // whole rows only (q8 divides the block)
-  const int64_t row = idx / q8;
-  const int d0 = (int)(idx % q8) * 8;
-  const int j = (int)(row % p.Sk);
-  const int hk = (int)((row / p.Sk) % p.n_rot_kv);
-  const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
+  const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (idx >= p.Sk * q8) return;  // whole rows only (q8 divides the block)
+  const int hk = (int)blockIdx.y, b = (int)blockIdx.z;
+  const int j = idx / q8;
+  const int d0 = (idx - j * q8) * 8;
+  const bool rot = hk < p.n_rotk;  // uniform over the block
+  // the key position first: its load is then in flight with the row's
+  const int pos = rot ? key_position(p, b, j) : 0;
+  const int64_t row = ((int64_t)b * p.n_rot_kv + hk) * p.Sk + j;
   const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + d0;
   uint16_t* dst = (uint16_t*)p.k_rot + row * p.D + d0;
-  const bool rot = hk < p.n_rotk;
   const int hd = p.D / 2;
   constexpr int NE = HALF ? 16 : 8;
   float x[NE];  // HALF: x[0..7] at d0 + e, x[8..15] at d0 + hd + e
-  {
-    const uint4 a0 = *(const uint4*)src;
-    const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = Elem<T>::to_f32((uint16_t)(w0[e / 2] >> (16 * (e & 1))));
-    if constexpr (HALF) {
-      const uint4 a1 = *(const uint4*)(src + hd);
-      const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 + e] = Elem<T>::to_f32((uint16_t)(w1[e / 2] >> (16 * (e & 1))));
-    }
+  const u32x4_t a0 = *(const u32x4_t*)src;
+  u32x4_t a1 = {0u, 0u, 0u, 0u};
+  if constexpr (HALF) a1 = *(const u32x4_t*)(src + hd);
+  // RMSNorm weights of the same elements (16-byte vectors, issued early)
+  const bool norm = p.k_norm_w != nullptr;
+  u32x4_t wv0 = {0u, 0u, 0u, 0u}, wv1 = wv0;
+  if (norm) {
+    const uint16_t* wp = (const uint16_t*)p.k_norm_w + d0;
+    wv0 = *(const u32x4_t*)wp;
+    if constexpr (HALF) wv1 = *(const u32x4_t*)(wp + hd);
   }
-  if (p.k_norm_w != nullptr) {
+  // the pairs' cos / sin from the table row of the position, read as 16-byte
+  // vectors issued before the row is waited for; a position past the table
+  // takes the direct formula at the use (same bits)
+  constexpr int NP = HALF ? 8 : 4;    // pairs of this thread
+  const int i0 = HALF ? d0 : d0 / 2;  // first pair index (a multiple of 4)
+  const bool in_tab = pos >= 0 && pos < p.rope_tab_len;
+  float4 tv[NP / 2];
+  if (rot) {
+    const float4* trow = (const float4*)(p.rope_tab + (size_t)(in_tab ? pos : 0) * (p.D / 2) + i0);
+#pragma unroll
+    for (int u = 0; u < NP / 2; ++u) tv[u] = trow[u];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = Elem<T>::to_f32((uint16_t)(a0[e / 2] >> (16 * (e & 1))));
+  if constexpr (HALF) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[8 + e] = Elem<T>::to_f32((uint16_t)(a1[e / 2] >> (16 * (e & 1))));
+  }
+  if (norm) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) ss = fmaf(x[e], x[e], ss);
     for (int off = q8 / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = rsqrtf(ss / (float)p.D + p.norm_eps);
-    const uint16_t* wp = (const uint16_t*)p.k_norm_w;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) x[e] = x[e] * inv * Elem<T>::to_f32(wp[(e < 8 ? d0 : d0 + hd) + (e & 7)]);
+    for (int e = 0; e < NE; ++e) {
+      const uint32_t w = (e < 8 ? wv0 : wv1)[(e & 7) / 2];
+      x[e] = x[e] * inv * Elem<T>::to_f32((uint16_t)(w >> (16 * (e & 1))));
+    }
   }
   if (rot) {
-    const int pos = key_position(p, b, j);
 #pragma unroll
-    for (int t = 0; t < (HALF ? 8 : 4); ++t) {
+    for (int t = 0; t < NP; ++t) {
       // pair: interleaved (x[2t], x[2t+1]) of pair index d0/2 + t; half
       // split (x[t], x[8+t]) of pair index d0 + t
       const int ia = HALF ? t : 2 * t, ic = HALF ? 8 + t : 2 * t + 1;
-      const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, pos, HALF ? d0 + t : d0 / 2 + t, p.D, p.rs);
+      float2 cs = (t & 1) ? make_float2(tv[t / 2].z, tv[t / 2].w) : make_float2(tv[t / 2].x, tv[t / 2].y);
+      if (__builtin_expect(!in_tab, 0)) cs = rope_cs_direct(pos, i0 + t, p.D, p.rs);
       const float a = x[ia], c = x[ic];
       x[ia] = fmaf(a, cs.x, -c * cs.y);
       x[ic] = fmaf(c, cs.x, a * cs.y);
@@ -1176,7 +1196,7 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
 // K heads that get RoPE, rotated into the workspace (reads the table and the
 // derived key positions written by the plan).
 hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
-  if (p.n_rot_kv > 0) {
+  if (p.n_rot_kv > 0 && p.Sk > 0 && p.B > 0) {
     const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
     if (p.dtype == 0) {
       const int rows_per_blk = 256 / (p.D / 2);
@@ -1184,13 +1204,13 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
       k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
     } else {
       const bool half = p.rope_style == 1;
-      const unsigned nblk = (unsigned)((nrows * (p.D / (half ? 16 : 8)) + 255) / 256);
+      const dim3 nblk((unsigned)((p.Sk * (p.D / (half ? 16 : 8)) + 255) / 256), (unsigned)p.n_rot_kv, (unsigned)p.B);
       if (p.dtype == 2) {
-        if (half) k_rotate16_kernel<BF16, true><<<dim3(nblk), dim3(256), 0, s>>>(p);
-        else k_rotate16_kernel<BF16, false><<<dim3(nblk), dim3(256), 0, s>>>(p);
+        if (half) k_rotate16_kernel<BF16, true><<<nblk, dim3(256), 0, s>>>(p);
+        else k_rotate16_kernel<BF16, false><<<nblk, dim3(256), 0, s>>>(p);
       } else {
-        if (half) k_rotate16_kernel<F16, true><<<dim3(nblk), dim3(256), 0, s>>>(p);
-        else k_rotate16_kernel<F16, false><<<dim3(nblk), dim3(256), 0, s>>>(p);
+        if (half) k_rotate16_kernel<F16, true><<<nblk, dim3(256), 0, s>>>(p);
+        else k_rotate16_kernel<F16, false><<<nblk, dim3(256), 0, s>>>(p);
       }
     }
   }
