@@ -108,21 +108,78 @@ def pmc_workload():
     print("pmc workload done", flush=True)
 
 
+TRAFFIC_KERNELS = (("fwd_mfma_kernel", "fwd_mfma_kernel"), ("k_rotate16_kernel", "k_rotate16_kernel"),
+                   ("decode_mfma_kernel", "decode_mfma_kernel"), ("decode_merge16_kernel", "decode_merge16_kernel"))
+SIMDS = 1024  # 256 compute units x 4 SIMDs
+XCDS = 8
+
+
+def _counter_rows(d):
+    """(kernel name, counter name, value) of every counter_collection.csv
+    row under a rocprofv3 output directory (one row per dispatch and
+    counter)."""
+    import csv
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        yield r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+
+
+def counters_from(d):
+    """Per-dispatch means of the counters of one rocprofv3 --pmc run of
+    pmc_workload, per kernel of the timed path, with the MFMA busy share
+    (MFMA-busy SIMD cycles over GPU-active cycles times the SIMD count), the
+    LDS bank-conflict share of LDS-active cycles, and the flop the MFMA ops
+    counter implies (512 per op)."""
+    acc = {}
+    for kname, cname, v in _counter_rows(d):
+        for key, pat in TRAFFIC_KERNELS:
+            if pat in kname:
+                acc.setdefault(key, {}).setdefault(cname, []).append(v)
+    # launch durations of the same run (its kernel trace)
+    import csv
+    dur = {}
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("kernel_trace.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        for key, pat in TRAFFIC_KERNELS:
+                            if pat in r["Kernel_Name"]:
+                                dur.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {"source_hash": kernel_source_hash(), "xcds": XCDS, "simds": SIMDS}
+    for key, cs in acc.items():
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        e = {c: round(v, 1) for c, v in m.items()}
+        e["dispatches"] = max(len(v) for v in cs.values())
+        if dur.get(key):
+            e["avg_duration_us"] = round(sum(dur[key]) / len(dur[key]) / 1e3, 2)
+        # GRBM_GUI_ACTIVE comes summed over the XCDs: per-XCD active cycles
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        if gui and dur.get(key):
+            e["gui_cycles_per_ns"] = round(gui / (sum(dur[key]) / len(dur[key])), 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and gui:
+            e["mfma_busy_pct"] = round(100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS), 2)
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
+            e["lds_bank_conflict_pct"] = round(100.0 * m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"], 3)
+        mops = sum(m.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+        if mops:
+            e["mfma_gflop"] = round(mops * 512 / 1e9, 3)
+        out[key] = e
+    return out
+
+
 def traffic_from(fetch_dir, write_dir):
     """HBM bytes per launch from two rocprofv3 --pmc runs of pmc_workload
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each divided by the
     factor the same counter shows for the copy kernel of known size."""
-    import csv
-
     def per_kernel(d, counter):
         vals = {}
-        for root, _, files in os.walk(d):
-            for fn in files:
-                if fn.endswith("counter_collection.csv"):
-                    with open(os.path.join(root, fn)) as f:
-                        for r in csv.DictReader(f):
-                            if r["Counter_Name"] == counter:
-                                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        for kname, cname, v in _counter_rows(d):
+            if cname == counter:
+                vals.setdefault(kname, []).append(v)
         return vals
 
     out = {"source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
@@ -133,12 +190,11 @@ def traffic_from(fetch_dir, write_dir):
             raise SystemExit(f"no copy kernel found for {counter} in {d}")
         factor = max(copy) * 1024.0 / COPY_BYTES
         out[counter.lower() + "_factor"] = round(factor, 4)
-        for key, pat in (("fwd_mfma_kernel", "fwd_mfma_kernel"), ("decode_mfma_kernel", "decode_mfma_kernel"),
-                         ("decode_merge16_kernel", "decode_merge16_kernel")):
+        for key, pat in TRAFFIC_KERNELS:
             vs = [v for k, v_ in vals.items() if pat in k for v in v_]
             if vs:
                 out.setdefault(key, {})[counter.lower() + "_bytes"] = round(sum(vs) / len(vs) * 1024.0 / factor)
-    for key in ("fwd_mfma_kernel", "decode_mfma_kernel", "decode_merge16_kernel"):
+    for key, _ in TRAFFIC_KERNELS:
         if key in out and "fetch_size_bytes" in out[key] and "write_size_bytes" in out[key]:
             out[key]["bytes"] = out[key]["fetch_size_bytes"] + out[key]["write_size_bytes"]
     return out
@@ -187,9 +243,14 @@ def main(argv=None):
                     help="run the short counter workload (under rocprofv3 --pmc) and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output dirs into traffic JSON on stdout and exit")
+    ap.add_argument("--counters-from", metavar="PMC_DIR",
+                    help="per-kernel counter means of one rocprofv3 --pmc output dir as JSON on stdout, and exit")
     a = ap.parse_args(argv)
     if a.traffic_from:
         print(json.dumps(traffic_from(*a.traffic_from), indent=1))
+        return 0
+    if a.counters_from:
+        print(json.dumps(counters_from(a.counters_from), indent=1))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

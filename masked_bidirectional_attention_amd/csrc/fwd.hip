@@ -175,11 +175,14 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
 // lanes, so the row's sum of squares (RMSNorm of k) is a reduction over
 // them.  Heads below n_rotk are rotated; all are normalised when k_norm_w
 // is set.  Grid: x over the Sk * q8 threads of one (batch, head) (32-bit
-// index math), y the K head, z the batch row.
+// index math), y the K head, z the batch row.  gridDim.x is a multiple of 8,
+// so block x runs on XCD x % 8 in every (head, batch) slab; the remap gives
+// each XCD one contiguous eighth of the key rows, and with it one eighth of
+// the cos/sin table rows in its L2 instead of most of the table.
 template <typename T, bool HALF>
 __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int q8 = HALF ? p.D / 16 : p.D / 8;
-  const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int idx = xcd_remap((int)blockIdx.x, (int)gridDim.x) * 256 + (int)threadIdx.x;
   if (idx >= p.Sk * q8) return;  // whole rows only (q8 divides the block)
   const int hk = (int)blockIdx.y, b = (int)blockIdx.z;
   const int j = idx / q8;
@@ -1204,7 +1207,8 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
       k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
     } else {
       const bool half = p.rope_style == 1;
-      const dim3 nblk((unsigned)((p.Sk * (p.D / (half ? 16 : 8)) + 255) / 256), (unsigned)p.n_rot_kv, (unsigned)p.B);
+      const unsigned nx = (unsigned)((p.Sk * (p.D / (half ? 16 : 8)) + 255) / 256);
+      const dim3 nblk((nx + 7) & ~7u, (unsigned)p.n_rot_kv, (unsigned)p.B);
       if (p.dtype == 2) {
         if (half) k_rotate16_kernel<BF16, true><<<nblk, dim3(256), 0, s>>>(p);
         else k_rotate16_kernel<BF16, false><<<nblk, dim3(256), 0, s>>>(p);
