@@ -263,16 +263,16 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
 }
 
 // fp32: one thread per pair; the D/2 threads of a row are adjacent lanes.
+// Grid as for the 16-bit pass: x over the key rows of one (batch, head), a
+// multiple of 8 remapped per XCD, y the K head, z the batch row.
 __global__ void k_rotate32_kernel(const FwdParams p) {
   const int half = p.D / 2;
-  const int rows_per_blk = blockDim.x / half;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_blk + threadIdx.x / half;
-  const int i = threadIdx.x % half;
-  const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
-  if (row >= nrows) return;  // whole rows only
-  const int j = (int)(row % p.Sk);
-  const int hk = (int)((row / p.Sk) % p.n_rot_kv);
-  const int b = (int)(row / ((int64_t)p.Sk * p.n_rot_kv));
+  const int rows_per_blk = 256 / half;
+  const int j = xcd_remap((int)blockIdx.x, (int)gridDim.x) * rows_per_blk + (int)threadIdx.x / half;
+  const int i = (int)threadIdx.x % half;
+  if (j >= p.Sk) return;  // whole rows only
+  const int hk = (int)blockIdx.y, b = (int)blockIdx.z;
+  const int64_t row = ((int64_t)b * p.n_rot_kv + hk) * p.Sk + j;
   // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
   const int d0 = p.rope_style == 1 ? i : 2 * i, d1 = p.rope_style == 1 ? i + half : 2 * i + 1;
   const float* src = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2];
@@ -1200,11 +1200,10 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
 // derived key positions written by the plan).
 hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
   if (p.n_rot_kv > 0 && p.Sk > 0 && p.B > 0) {
-    const int64_t nrows = (int64_t)p.B * p.n_rot_kv * p.Sk;
     if (p.dtype == 0) {
       const int rows_per_blk = 256 / (p.D / 2);
-      const unsigned nblk = (unsigned)((nrows + rows_per_blk - 1) / rows_per_blk);
-      k_rotate32_kernel<<<dim3(nblk), dim3(256), 0, s>>>(p);
+      const unsigned nx = (unsigned)((p.Sk + rows_per_blk - 1) / rows_per_blk);
+      k_rotate32_kernel<<<dim3((nx + 7) & ~7u, (unsigned)p.n_rot_kv, (unsigned)p.B), dim3(256), 0, s>>>(p);
     } else {
       const bool half = p.rope_style == 1;
       const unsigned nx = (unsigned)((p.Sk * (p.D / (half ? 16 : 8)) + 255) / 256);
