@@ -522,7 +522,7 @@ def main(argv=None):
             "value": round(gbs, 1),
             "unit": "GB/s",
             "roofline": {
-                "kernel": "decode_mfma_kernel<bf16,128,1>",
+                "kernel": "whole decode call: decode_mfma_kernel<bf16,128,1> + decode_merge16_kernel<bf16,128>",
                 "bound": "hbm",
                 "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS,

@@ -300,7 +300,7 @@ def _mask_strides(m, B, H, Sq, Sk, name="mask"):
             st.append(0 if i < 3 else m.stride(i))
         else:
             raise MzattnError(MZ_ERR_SHAPE, f"{name} dim {i} is {m.shape[i]}, expected {want[i]} or 1")
-    if Sk == 1:
+    if Sk <= 1:
         st[3] = 1
     return m, _i64x4(*st)
 
@@ -332,13 +332,18 @@ class FwdCall:
     """A marshalled forward call: the C argument struct plus the tensors it
     points to (kept alive here).  ``plan()`` launches the layout prepasses,
     ``execute()`` the per-input work (``rotate_k()`` then ``attend()``), all
-    on the call's stream; ``__call__`` launches everything."""
+    on the call's stream; ``__call__`` launches everything.
+
+    The plan lives in the workspace, so every FwdCall owns one (allocated
+    here unless ``workspace`` is given): a plan is never overwritten by
+    another call's.  A caller-supplied workspace must not be shared with
+    another call between its plan and its executes."""
 
     def __init__(self, q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                  rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
                  rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6,
-                 out=None, return_lse: bool = False, workspace=None, stream=None):
+                 out=None, return_lse: bool = False, workspace=None, stream=None, _shared_workspace=False):
         torch = _torch()
         L = lib()
         B, Hq, Sq, D = q.shape
@@ -399,8 +404,13 @@ class FwdCall:
         _check(L.mzattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
         self.stream = torch.cuda.current_stream(q.device) if stream is None else stream
         if need.value > 0:
-            if workspace is None:
+            if workspace is None and _shared_workspace:
+                # one-shot calls (plan and execute launched back to back on
+                # one stream) share a per-stream buffer: stream order keeps
+                # a later call from overwriting it before this one is done
                 workspace = _WS.get("fwd", q.device, self.stream.cuda_stream, need.value, zero=False)
+            elif workspace is None:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
             a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
             keep.append(workspace)
         self.args, self.out, self._keep, self._lib = a, o, keep, L
@@ -449,7 +459,7 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = Fal
                    scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, rope_precision=rope_precision,
                    rope_mscale=rope_mscale, rope_factors=rope_factors, q_norm_weight=q_norm_weight,
                    k_norm_weight=k_norm_weight, norm_eps=norm_eps, out=out,
-                   return_lse=return_lse, workspace=workspace, stream=stream)()
+                   return_lse=return_lse, workspace=workspace, stream=stream, _shared_workspace=True)()
 
 
 class DecodeCall:

@@ -134,7 +134,9 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
   pl->empty = a->batch == 0 || a->seq_q == 0;
 
   if (a->mask_kind == MZ_MASK_BOOL) {
-    if (a->mask_stride[3] != 1) return fail(MZ_ERR_STRIDE, "mask_stride[3] must be 1 (got %lld)", (long long)a->mask_stride[3]);
+    // (with no keys the mask is never read)
+    if (a->mask_stride[3] != 1 && a->seq_k > 0)
+      return fail(MZ_ERR_STRIDE, "mask_stride[3] must be 1 (got %lld)", (long long)a->mask_stride[3]);
     for (int i = 0; i < 3; ++i)
       if (a->mask_stride[i] < 0) return fail(MZ_ERR_STRIDE, "mask_stride[%d] is negative", i);
     pl->Bm = a->mask_stride[0] == 0 ? 1 : a->batch;
@@ -199,7 +201,8 @@ int validate_fwd_full(const mzattn_fwd_args* a, FwdPlan* pl) {
   if (a->k_stride[2] >= (int64_t(1) << 24) || a->v_stride[2] >= (int64_t(1) << 24))
     return fail(MZ_ERR_UNSUPPORTED, "k / v row strides must be below 2^24 elements");
   if (a->pos_q_stride_b < 0 || a->pos_k_stride_b < 0) return fail(MZ_ERR_STRIDE, "position strides must be >= 0");
-  if (a->mask_kind == MZ_MASK_BOOL && a->mask == nullptr) return fail(MZ_ERR_NULL, "mask_kind BOOL needs mask");
+  if (a->mask_kind == MZ_MASK_BOOL && a->mask == nullptr && a->seq_k > 0)
+    return fail(MZ_ERR_NULL, "mask_kind BOOL needs mask");
   if (a->mask_kind == MZ_MASK_SEGMENT) {
     if (a->seg_q == nullptr || (a->seg_k == nullptr && a->seq_k > 0))
       return fail(MZ_ERR_NULL, "mask_kind SEGMENT needs seg_q and seg_k");

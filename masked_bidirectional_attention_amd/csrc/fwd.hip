@@ -1190,8 +1190,9 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
     seg_prep_kernel<<<dim3(p.n_qt > nkb ? p.n_qt : nkb, p.B), dim3(256), 0, s>>>(p, bm);
   }
   if (p.mask_kind == 1) {
+    // (no key tiles: nothing to classify; the attention kernel visits none)
     const int64_t ntiles = (int64_t)p.Bm * p.Hm * p.n_qt * p.n_kt;
-    mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
+    if (ntiles > 0) mask_tiles_kernel<<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(p, bm);
   }
   return hipGetLastError();
 }

@@ -2,6 +2,9 @@
 library (via the C-ABI binding) and through the fp64 oracle."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -67,11 +70,22 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def log_parity(record: dict):
+    """Append one JSON line to the file named by MZATTN_PARITY_LOG (if set):
+    the achieved error of a parity check, kept beside the pass/fail."""
+    path = os.environ.get("MZATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(record) + "\n")
+
+
 def assert_parity(dtype, out, ref, what=""):
     st = mzref.parity_stats(to64(out), ref)
     print(f"[parity] {what} {dtype} max_abs={st['max_abs']:.3e} rel_l2={st['rel_l2']:.3e} "
           f"max_ref={st['max_ref']:.3g}", flush=True)
-    assert mzref.within_tolerance(dtype, st), f"{what}: out of tolerance {st}"
+    ok = mzref.within_tolerance(dtype, st)
+    log_parity({"what": what, "dtype": dtype, "ok": ok, **st})
+    assert ok, f"{what}: out of tolerance {st}"
     return st
 
 

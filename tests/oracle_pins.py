@@ -622,6 +622,77 @@ def pin_qk_rms_norm():
     _close(o2, o3, 1e-12, "rms norm scale invariance")
 
 
+# --------------------------------------------------------------------------
+# the comparison that decides every GPU parity verdict
+# --------------------------------------------------------------------------
+
+
+def pin_parity_checker():
+    """``parity_stats`` / ``within_tolerance`` on synthetic outputs placed
+    just inside and just outside each bound the GPU path is held to: fp32
+    max |d| <= 1e-5; fp16 / bf16 relative L2 <= 4e-3 and max |d| <=
+    2e-2 * max |ref| (both must hold); non-finite outputs fail; an
+    all-zero reference admits only an all-zero output.  The bounds are the
+    stated tolerances, so the margins here (a few tenths of a percent) are
+    what a slip in the checker (an ``or`` for the ``and``, the norm or the
+    maximum taken from the output instead of the reference, a bound off by
+    a factor) has to survive."""
+    rng = np.random.default_rng(97)
+    ok = lambda dt, out, ref: mzref.within_tolerance(dt, mzref.parity_stats(out, ref))
+    ref = rng.standard_normal(4096)
+    # fp32: one element off by just under / just over 1e-5 (max |d| only)
+    for d, want in ((0.99e-5, True), (1.01e-5, False), (-1.01e-5, False)):
+        out = ref.copy()
+        out[17] += d
+        assert ok("f32", out, ref) is want, f"f32 bump {d}"
+    # fp32: a rel-L2 far above 4e-3 with max |d| below 1e-5 still passes
+    small = rng.standard_normal(64) * 1e-3
+    out = small + 0.9e-5
+    st = mzref.parity_stats(out, small)
+    assert st["rel_l2"] > 4e-3 and ok("f32", out, small), "f32 holds max |d| only"
+    for dt in ("bf16", "f16"):
+        # relative L2 just under / just over 4e-3 (max |d| well inside)
+        for eps, want in ((3.99e-3, True), (4.005e-3, False)):
+            out = ref * (1.0 + eps)
+            st = mzref.parity_stats(out, ref)
+            assert abs(st["rel_l2"] - eps) < 1e-9, f"rel_l2 {st['rel_l2']} != {eps}"
+            assert ok(dt, out, ref) is want, f"{dt} rel-L2 {eps}"
+        # max |d| just under / just over 2e-2 * max |ref| at the largest
+        # element, rel-L2 well inside (a long all-ones reference)
+        big = np.ones(200000)
+        big[5] = 2.0
+        for frac, want in ((0.0198, True), (0.0202, False)):
+            out = big.copy()
+            out[5] += frac * 2.0
+            st = mzref.parity_stats(out, big)
+            assert st["rel_l2"] < 1e-3 and st["max_ref"] == 2.0
+            assert ok(dt, out, big) is want, f"{dt} max-abs {frac}"
+        # the same bump on an ordinary element is judged against max |ref|
+        out = big.copy()
+        out[9] += 0.0202 * 2.0
+        assert not ok(dt, out, big), f"{dt} max-abs on a non-maximal element"
+        # non-finite outputs fail however small the rest of the error
+        for bad in (np.nan, np.inf, -np.inf):
+            out = ref.copy()
+            out[3] = bad
+            assert not ok(dt, out, ref), f"{dt} output {bad}"
+        # an all-zero reference: zero passes, anything else fails
+        z = np.zeros(256)
+        assert ok(dt, z.copy(), z)
+        out = z.copy()
+        out[0] = 1e-6
+        assert not ok(dt, out, z), f"{dt} nonzero output for a zero reference"
+    for bad in (np.nan, np.inf):
+        out = ref.copy()
+        out[3] = bad
+        assert not ok("f32", out, ref), f"f32 output {bad}"
+    # empty outputs (no queries) pass
+    assert ok("bf16", np.zeros(0), np.zeros(0)) and ok("f32", np.zeros(0), np.zeros(0))
+    # the statistics themselves, on a hand-checked case
+    st = mzref.parity_stats(np.array([3.0, 4.0, 0.0]), np.array([0.0, 0.0, -2.0]))
+    assert st["max_abs"] == 4.0 and st["max_ref"] == 2.0 and abs(st["rel_l2"] - math.sqrt(29.0) / 2.0) < 1e-15
+
+
 ALL_PINS = [
     pin_fp16_decode, pin_bf16_decode, pin_fp32_decode,
     pin_rope_complex_form, pin_rope_hand_values, pin_rope_properties,
@@ -634,5 +705,5 @@ ALL_PINS = [
     pin_append_empty_cache_is_causal_sdpa, pin_append_single_token_first_row,
     pin_append_equals_sdpa_on_updated_cache, pin_append_overflow,
     pin_longrope_vs_transformers, pin_rope_fp16_angles_vs_torch, pin_rope_bf16_table_vs_torch,
-    pin_qk_rms_norm,
+    pin_qk_rms_norm, pin_parity_checker,
 ]

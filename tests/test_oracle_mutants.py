@@ -70,6 +70,18 @@ MUTANTS = {
                              "kh = rms_norm(kh, decode(q_norm_w, dtype), norm_eps)"),
     "causal_transposed": ("live = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]",
                           "live = np.arange(Sk)[None, :] >= np.arange(Sq)[:, None]"),
+    # the parity checker (parity_stats / within_tolerance)
+    "checker_or_for_and": ('return stats["rel_l2"] <= 4e-3 and stats["max_abs"]',
+                           'return stats["rel_l2"] <= 4e-3 or stats["max_abs"]'),
+    "checker_norm_of_out": ("nref = float(np.linalg.norm(ref))", "nref = float(np.linalg.norm(out))"),
+    "checker_max_ref_of_out": ('"max_ref": float(np.abs(ref).max())', '"max_ref": float(np.abs(out).max())'),
+    "checker_f32_bound_1e4": ('return stats["max_abs"] <= 1e-5', 'return stats["max_abs"] <= 1e-4'),
+    "checker_f32_as_16bit": ('if dtype == "f32":\n        return stats["max_abs"] <= 1e-5',
+                             'if dtype == "fp32":\n        return stats["max_abs"] <= 1e-5'),
+    "checker_rel_bound_4e2": ('stats["rel_l2"] <= 4e-3', 'stats["rel_l2"] <= 4e-2'),
+    "checker_abs_factor_0_2": ('stats["max_abs"] <= 2e-2 * max', 'stats["max_abs"] <= 2e-1 * max'),
+    "checker_mean_abs": ('"max_abs": float(np.abs(d).max())', '"max_abs": float(np.abs(d).mean())'),
+    "checker_abs_floor_1": ('max(stats["max_ref"], 1e-30)', 'max(stats["max_ref"], 1.0)'),
 }
 
 

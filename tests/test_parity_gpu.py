@@ -11,7 +11,7 @@ import torch
 
 from masked_bidirectional_attention_amd import workloads as W
 from oracle import mzref
-from tests.gpu_helpers import (DEV, assert_parity, bits, dev, oracle_decode, oracle_fwd, run_decode,
+from tests.gpu_helpers import (DEV, assert_parity, bits, dev, log_parity, oracle_decode, oracle_fwd, run_decode,
                                run_fwd, to64)
 
 pytestmark = pytest.mark.gpu
@@ -68,9 +68,16 @@ def test_packed_equals_separate_rows():
     S, U = W.QWEN_S, W.QWEN_UNCOND
     a = torch.cat([o2[0:1], o2[1:2, :, :U]], dim=2)
     st = mzref.parity_stats(to64(op), to64(a))
-    print(f"[packed vs padded] max_abs={st['max_abs']:.3e} rel_l2={st['rel_l2']:.3e} "
-          f"bitwise={torch.equal(op, a)}", flush=True)
+    same = torch.equal(op, a)
+    print(f"[packed vs padded] max_abs={st['max_abs']:.3e} rel_l2={st['rel_l2']:.3e} bitwise={same}", flush=True)
+    log_parity({"what": "packed vs padded rows", "bitwise": same, **st})
     assert mzref.within_tolerance("bf16", st)
+    # Both segments start on query-tile (128) and key-tile (64) boundaries,
+    # the K rotation and the cos / sin rows are the same for the same
+    # positions, and keys past the segment end are excluded by a select in
+    # both forms (zeros read past the row end, masked keys in the padded
+    # row), so every output takes the same operations in the same order.
+    assert same, "packed row differs from the separate rows"
 
 
 @pytest.mark.parametrize("filled", W.VOX_FILLED)
@@ -322,6 +329,11 @@ def test_fully_masked_and_empty():
     # no queries: a legal no-op
     z = W.random_fwd(26, 1, 2, 2, 0, 10, 64, "bf16")
     assert run_fwd(z).shape == (1, 2, 0, 64)
+    # no keys under a boolean mask (the mask itself is empty): zeros, lse -inf
+    for dtype in ("bf16", "f32"):
+        eb = W.random_fwd(25, 2, 2, 2, 10, 0, 64, dtype, W.MASK_BOOL, mask_shape="key")
+        ob, lb = run_fwd(eb, return_lse=True)
+        assert ob.shape == (2, 2, 10, 64) and torch.all(ob == 0) and torch.all(torch.isinf(lb))
 
 
 def test_deterministic():
@@ -377,6 +389,72 @@ def test_plan_then_execute_equals_fwd():
     assert torch.equal(call.out, b2)
 
 
+def test_plan_survives_other_calls_on_the_stream():
+    """A planned call keeps its plan while other calls (one-shot and
+    planned, with other masks and shapes) run on the same stream between
+    its plan and its executes."""
+    import masked_bidirectional_attention_amd as mz
+    a = W.random_fwd(34, 2, 8, 2, 300, 400, 128, "bf16", W.MASK_BOOL, mask_shape="blocky", rope_base=1e6)
+    b = W.random_fwd(35, 2, 8, 2, 300, 400, 128, "bf16", W.MASK_BOOL, mask_shape="full", rope_base=1e4)
+    c = W.random_fwd(36, 1, 8, 2, 257, 257, 128, "bf16", W.MASK_SEGMENT, rope_base=1e6, n_segments=3)
+    call_a = mz.FwdCall(dev(a.q), dev(a.k), dev(a.v), mask=dev(a.mask), rope_base=a.rope_base)
+    call_a.plan()
+    run_fwd(b)                      # one-shot call in between
+    run_fwd(c)
+    call_b = mz.FwdCall(dev(b.q), dev(b.k), dev(b.v), mask=dev(b.mask), rope_base=b.rope_base)
+    call_b.plan()                   # another plan in between
+    call_a.execute()
+    call_b.execute()
+    torch.cuda.synchronize()
+    ref_a, _ = oracle_fwd(a)
+    assert_parity("bf16", call_a.out, ref_a, "plan kept across other calls")
+    ref_b, _ = oracle_fwd(b)
+    assert_parity("bf16", call_b.out, ref_b, "second planned call")
+
+
+def _segment_rows(rng, B, S, ids, pad_front):
+    """Non-decreasing id rows of length S over the given ids (random run
+    lengths), with an optional run of padding (-1) in front."""
+    rows = []
+    for b in range(B):
+        cuts = np.sort(rng.choice(np.arange(1, S), size=len(ids) - 1, replace=False))
+        row = np.full(S, ids[0], dtype=np.int32)
+        for c, v in zip(cuts, ids[1:]):
+            row[c:] = v
+        if pad_front and b == 0:
+            row[:int(rng.integers(1, S // 6))] = -1
+        rows.append(row)
+    return torch.from_numpy(np.stack(rows))
+
+
+@pytest.mark.parametrize("cfg", [
+    # B, Hq, Hkv, Sq, Sk, D, dtype, query ids, key ids
+    (2, 4, 2, 300, 500, 128, "bf16", [0, 1, 2], [0, 1, 2, 3]),
+    (1, 2, 2, 260, 130, 64, "f16", [0, 2, 3], [0, 1, 2]),
+    (2, 2, 1, 100, 170, 64, "f32", [1, 2], [0, 1, 2]),
+], ids=lambda c: f"{c[3]}x{c[4]}-{c[6]}")
+def test_segment_rows_of_different_lengths(cfg):
+    """Segment mode with seq_q != seq_k and distinct id rows: query i and
+    key j are live together iff their ids are equal and >= 0; positions
+    restart at 0 in every run on each axis separately.  Ids present on one
+    axis only leave their queries with no live key (zero output)."""
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, Sq, Sk, D, dtype, qids, kids = cfg
+    rng = np.random.default_rng(zlib.crc32(repr(cfg).encode()) % 10000)
+    case = W.random_fwd(int(rng.integers(1 << 20)), B, Hq, Hkv, Sq, Sk, D, dtype, rope_base=1e4)
+    sq = _segment_rows(rng, B, Sq, qids, pad_front=True)
+    sk = _segment_rows(rng, B, Sk, kids, pad_front=False)
+    o, lse = mz.mzattn_fwd(dev(case.q), dev(case.k), dev(case.v), seg_q=dev(sq), seg_k=dev(sk), rope_base=1e4,
+                           return_lse=True)
+    torch.cuda.synchronize()
+    ref, lse_ref = mzref.mzref_fwd(dtype, W.to_bits(case.q), W.to_bits(case.k), W.to_bits(case.v), rope_base=1e4,
+                                   mask_kind="segment", seg_q=sq.numpy(), seg_k=sk.numpy())
+    assert_parity(dtype, o, ref, f"segments {Sq}x{Sk}")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(to64(lse)), fin) and not fin.all()
+    np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=1e-4 if dtype == "f32" else 3e-2)
+
+
 @pytest.mark.parametrize("S", [4096, 5000])
 def test_long_segment_rows_fwd(S):
     """Segment rows longer than the LDS search buffer take the global path."""
@@ -427,17 +505,31 @@ def test_decode_no_mask(dtype, shape):
     assert_parity(dtype, o, oracle_decode(case), f"decode no mask {shape}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_decode_long_cache(dtype):
+    """A cache of 547 chunks (the merge folds nine super-groups of 64, the
+    last ragged): parity, and the span cut past the last live key changes
+    no bit."""
+    case = W.random_decode(71, 2, 8, 1, 2, 70000, 64, dtype, filled=68001, span=70000, mask_heads=True)
+    o = run_decode(case)
+    assert_parity(dtype, o, oracle_decode(case), f"long cache {dtype}")
+    o_cut = run_decode(case, span=W.ceil256(68001))
+    assert np.array_equal(bits(o), bits(o_cut)), "span truncation changed bits"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_repeated_calls_share_workspace(dtype):
-    """Calls of several shapes and spans through one workspace that starts
-    as all-ones bytes (NaN as floats), each checked against the oracle:
-    nothing a call reads from the workspace may be left from before it."""
+    """Calls of several shapes and spans (one chunk to 71 chunks, 1 to 4
+    query rows per head) through one workspace that starts as all-ones
+    bytes (NaN as floats), each checked against the oracle: nothing a call
+    reads from the workspace may be left from before it."""
     import masked_bidirectional_attention_amd as mz
-    cases = [W.random_decode(60 + i, B, Hq, Hkv, 1, C, 128, dtype, fill, span)
-             for i, (B, Hq, Hkv, C, fill, span) in enumerate([
-                 (2, 16, 2, 4096, 3000, 4096), (2, 16, 2, 4096, 3000, 3072), (1, 8, 1, 4096, 200, 256),
-                 (2, 16, 2, 4096, 4096, 4096), (2, 16, 2, 4096, 3000, 4096)])]
-    ws = torch.full((16 << 20,), 255, dtype=torch.uint8, device=dev(torch.zeros(1)).device)
+    cases = [W.random_decode(60 + i, B, Hq, Hkv, T, C, 128, dtype, fill, span)
+             for i, (B, Hq, Hkv, T, C, fill, span) in enumerate([
+                 (2, 16, 2, 1, 4096, 3000, 4096), (2, 16, 2, 1, 4096, 3000, 3072), (1, 8, 1, 1, 4096, 200, 256),
+                 (2, 16, 2, 1, 4096, 4096, 4096), (3, 8, 1, 2, 1500, 1400, 1408), (1, 4, 4, 1, 100, 100, 100),
+                 (4, 16, 4, 1, 9000, 8800, 8960), (2, 16, 2, 1, 4096, 3000, 4096)])]
+    ws = torch.full((16 << 20,), 255, dtype=torch.uint8, device=DEV)
     for rep in range(2):
         for c in cases:
             call = mz.DecodeCall(dev(c.q), dev(c.k_cache), dev(c.v_cache), span=c.span, mask=dev(c.mask),
