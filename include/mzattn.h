@@ -263,6 +263,21 @@ int mzattn_decode(const mzattn_decode_args* args, void* stream);
 int mzattn_decode_workspace_size(const mzattn_decode_args* args, size_t* bytes);
 int mzattn_validate_decode(const mzattn_decode_args* args);
 
+/* mzattn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, kernels and result as mzattn_decode, except that
+ * args->workspace and args->workspace_bytes are ignored: the partials go
+ * to a device array of MZATTN_NOALLOC_SCRATCH_BYTES bytes inside this
+ * library, one per GPU, which each GPU holds from its first call until the
+ * process ends.  A step whose mzattn_decode_workspace_size() exceeds that
+ * size is rejected with MZ_ERR_WORKSPACE before anything is launched.  The
+ * call allocates and frees nothing.  Every call on one GPU uses that GPU's
+ * array (its contents need no initialisation; each call writes what it
+ * reads), so calls on one GPU that overlap in time (other streams, other
+ * threads) race and must be serialised by the caller. */
+#define MZATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mzattn_decode_noalloc(const mzattn_decode_args* args, void* stream);
+
 /* ---- mzattn_decode_append ---------------------------------------------- */
 /*
  * One generation step that appends its own keys and values to the static

@@ -15,7 +15,8 @@ from ._binding import (  # noqa: F401
     lib,
     mzattn_decode,
     mzattn_decode_append,
+    mzattn_decode_noalloc,
     mzattn_fwd,
 )
 
-__all__ = ["DecodeCall", "DecodeAppendCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "mzattn_decode_append", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]
+__all__ = ["DecodeCall", "DecodeAppendCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "mzattn_decode_append", "mzattn_decode_noalloc", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]

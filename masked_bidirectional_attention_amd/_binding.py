@@ -201,6 +201,7 @@ _SIGNATURES = {
     "mzattn_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "mzattn_decode_workspace_size": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "mzattn_validate_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs)]),
+    "mzattn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]),
     "mzattn_decode_append": (ctypes.c_int, [ctypes.POINTER(DecodeAppendArgs), ctypes.c_void_p]),
     "mzattn_decode_append_workspace_size": (ctypes.c_int, [ctypes.POINTER(DecodeAppendArgs),
                                                            ctypes.POINTER(ctypes.c_size_t)]),
@@ -465,12 +466,14 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = Fal
 class DecodeCall:
     """A marshalled static-cache step: the C argument struct plus the
     tensors it points to.  ``set_cache`` swaps in other caches of the same
-    shape, strides and dtype; ``__call__`` launches on the call's stream."""
+    shape, strides and dtype; ``__call__`` launches on the call's stream.
+    With ``noalloc`` the call goes to ``mzattn_decode_noalloc`` (the
+    library's own per-GPU scratch; no workspace is allocated here)."""
 
     def __init__(self, q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
                  scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
                  rope_precision: str = "exact", rope_mscale: float = 0.0, rope_factors=None, out=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, noalloc: bool = False):
         torch = _torch()
         L = lib()
         B, Hq, T, D = q.shape
@@ -503,10 +506,12 @@ class DecodeCall:
         need = ctypes.c_size_t(0)
         _check(L.mzattn_decode_workspace_size(ctypes.byref(a), ctypes.byref(need)))
         self.stream = torch.cuda.current_stream(q.device) if stream is None else stream
-        if workspace is None:
-            workspace = _WS.get("decode", q.device, self.stream.cuda_stream, need.value, zero=False)
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        keep.append(workspace)
+        self._fn = L.mzattn_decode_noalloc if noalloc else L.mzattn_decode
+        if not noalloc:
+            if workspace is None:
+                workspace = _WS.get("decode", q.device, self.stream.cuda_stream, need.value, zero=False)
+            a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+            keep.append(workspace)
         self.args, self.out, self._keep, self._lib = a, o, keep, L
         self._cache_shape = (tuple(k_cache.shape), tuple(k_cache.stride()), k_cache.dtype)
 
@@ -518,7 +523,7 @@ class DecodeCall:
         self._keep[1], self._keep[2] = k_cache, v_cache
 
     def __call__(self):
-        _check(self._lib.mzattn_decode(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
+        _check(self._fn(ctypes.byref(self.args), ctypes.c_void_p(self.stream.cuda_stream)))
         return self.out
 
 
@@ -532,6 +537,18 @@ def mzattn_decode(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
     return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
                       q_pos=q_pos, rope_style=rope_style, rope_precision=rope_precision,
                       rope_mscale=rope_mscale, rope_factors=rope_factors, out=out, workspace=workspace, stream=stream)()
+
+
+def mzattn_decode_noalloc(q, k_cache, v_cache, *, span: Optional[int] = None, mask=None,
+                          scale: float = 0.0, rope_base: float = 0.0, q_pos=None, rope_style: str = "interleaved",
+                          rope_precision: str = "exact", rope_mscale: float = 0.0, rope_factors=None, out=None,
+                          stream=None):
+    """``mzattn_decode`` through ``mzattn_decode_noalloc``: the library's
+    fixed per-GPU scratch replaces the workspace (include/mzattn.h).  Calls
+    on one GPU must not overlap in time."""
+    return DecodeCall(q, k_cache, v_cache, span=span, mask=mask, scale=scale, rope_base=rope_base,
+                      q_pos=q_pos, rope_style=rope_style, rope_precision=rope_precision,
+                      rope_mscale=rope_mscale, rope_factors=rope_factors, out=out, stream=stream, noalloc=True)()
 
 
 class DecodeAppendCall:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "mzattn.h"
@@ -369,6 +370,8 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   p.lse = a->lse;
 }
 
+int run_decode(const mzattn_decode_args* a, void* stream);
+
 enum { FWD_PLAN = 1, FWD_ROT = 2, FWD_MAIN = 4 };
 
 int run_fwd(const mzattn_fwd_args* a, void* stream, int parts) {
@@ -453,7 +456,77 @@ int mzattn_validate_decode(const mzattn_decode_args* args) {
   return st == MZ_OK ? ok() : st;
 }
 
-int mzattn_decode(const mzattn_decode_args* a, void* stream) {
+int mzattn_decode(const mzattn_decode_args* a, void* stream) { return run_decode(a, stream); }
+
+}  // extern "C"
+
+// ---- the decode step without allocation --------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): mzattn_decode with the
+// workspace taken from a fixed device array of this library instead of the
+// caller.  Each GPU holds its own copy of the array until the process ends;
+// its device address is looked up once per device and kept, and only that
+// address is handed to the kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(MZATTN_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on the first
+// call on the device, with that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MZ_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MZ_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MZ_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mzattn_decode_noalloc(const mzattn_decode_args* a, void* stream) {
+  if (a == nullptr) return fail(MZ_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(mzattn_decode_args))
+    return fail(MZ_ERR_ABI, "struct_size %u != sizeof(mzattn_decode_args) %zu", a->struct_size,
+                sizeof(mzattn_decode_args));
+  DecPlan pl;
+  const int st = plan_decode(a, &pl);
+  if (st != MZ_OK) return st;
+  if (pl.bytes > kScratchBytes)
+    return fail(MZ_ERR_WORKSPACE, "the step needs %zu bytes of scratch, above the %zu this entry point holds",
+                pl.bytes, kScratchBytes);
+  mzattn_decode_args d = *a;
+  const int sa = scratch_address(&d.workspace);
+  if (sa != MZ_OK) return sa;
+  d.workspace_bytes = kScratchBytes;
+  return run_decode(&d, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_decode(const mzattn_decode_args* a, void* stream) {
   DecPlan pl;
   const int st = validate_decode_full(a, &pl);
   if (st != MZ_OK) return st;
@@ -493,7 +566,7 @@ int mzattn_decode(const mzattn_decode_args* a, void* stream) {
   return ok();
 }
 
-}  // extern "C"
+}  // namespace
 
 // ---- decode with append ---------------------------------------------------
 namespace {
