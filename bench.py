@@ -200,7 +200,23 @@ def traffic_from(fetch_dir, write_dir):
     return out
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline():
+    """The fp64 numpy oracle (never tuned for speed) on the host, on a
+    bounded sample of the packed-guidance workload: the full forward with
+    every BLAS thread (nproc) and a 2-head slice single-threaded, each the
+    median of 3 timed runs, scaled to live TFLOP/s."""
+    import statistics
     import threadpoolctl
     from masked_bidirectional_attention_amd import workloads as W
     from oracle import mzref
@@ -208,25 +224,35 @@ def cpu_baseline():
     c = W.qwen_cfg_packed()
     bq, bk, bv = W.to_bits(c.q), W.to_bits(c.k), W.to_bits(c.v)
     seg = c.seg_q.numpy()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:  # repeat the call until about 10 s of host work
-        mzref.mzref_fwd(c.dtype, bq, bk, bv, rope_base=c.rope_base, mask_kind="segment", seg_q=seg, seg_k=seg)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 50:
-            break
-    threads = 0
-    for info in threadpoolctl.threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 0)))
+
+    def run(heads):
+        t0 = time.perf_counter()
+        mzref.mzref_fwd(c.dtype, bq, bk, bv, rope_base=c.rope_base, mask_kind="segment", seg_q=seg, seg_k=seg,
+                        heads=heads)
+        return time.perf_counter() - t0
+
+    nproc = os.cpu_count() or 1
+    with threadpoolctl.threadpool_limits(limits=nproc, user_api="blas"):
+        threads = max([i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                       if i.get("user_api") == "blas"] or [nproc])
+        multi = statistics.median(run(None) for _ in range(3))
+    sub = [0, 9]   # one head of each K/V pair kind: heads 0 and 9 read K/V heads 0 and 4
+    with threadpoolctl.threadpool_limits(limits=1, user_api="blas"):
+        single = statistics.median(run(sub) for _ in range(3))
+    f_full = fwd_flops()
+    f_sub = f_full * len(sub) / 16
     return {
-        "value": fwd_flops() * reps / dt / 1e12,
+        "value": f_full / multi / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads or os.cpu_count(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} full packed-guidance forwards (16 heads, 2848 tokens, {fwd_flops() / 1e9:.2f} "
-                  f"live GFLOP each) through the fp64 numpy oracle: {dt:.2f} s",
+        "sample": f"packed-guidance forward (16 heads, 2848 tokens, {f_full / 1e9:.2f} live GFLOP) through the fp64 "
+                  f"numpy oracle with {threads} BLAS threads: median of 3 runs {multi:.2f} s",
+        "single_thread": {"value": f_sub / single / 1e12, "unit": "TFLOP/s", "cores": 1,
+                          "sample": f"heads {sub} of the same forward ({f_sub / 1e9:.2f} live GFLOP), one BLAS "
+                                    f"thread: median of 3 runs {single:.2f} s"},
+        "nproc": nproc,
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -341,6 +367,8 @@ def main(argv=None):
         mask_l = torch.zeros_like(dmask)
         mask_l[..., :L] = True
         for span in (8192, W.ceil256(L)):
+            # eager (events around each call, host launch included) and as a
+            # replayed graph of 8 calls over 8 cold cache copies (GPU time)
             dl = mz.DecodeCall(dq, kc0, vc0, span=span, mask=mask_l, scale=c4.scale)
             n = 50
             for i in range(5):
@@ -356,8 +384,27 @@ def main(argv=None):
                 torch.cuda.synchronize()
                 tot += e0.elapsed_time(e1)
             us = tot / n * 1e3
-            by_fill.append({"fill": L, "span": span, "us": round(us, 2),
+            gs = torch.cuda.Stream()
+            gcalls = [mz.DecodeCall(dq, kc, vc, span=span, mask=mask_l, scale=c4.scale, stream=gs)
+                      for kc, vc in copies[:8]]
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                for c_ in gcalls:
+                    c_()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(6):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            gus = e0.elapsed_time(e1) / (6 * 8) * 1e3
+            del g
+            by_fill.append({"fill": L, "span": span, "us": round(us, 2), "graph_us": round(gus, 2),
                             "GB/s": round(decode_bytes(L, span) / (us * 1e-6) / 1e9, 1),
+                            "GB/s_graph": round(decode_bytes(L, span) / (gus * 1e-6) / 1e9, 1),
                             "algorithmic_mb": round(decode_bytes(L, span) / 1e6, 3)})
     # ---- causal prefill (reported, not the headline): the same kernel under
     # the causal kind, K rotation + attention per call, layout planned once
@@ -381,6 +428,51 @@ def main(argv=None):
               "execute_us": round(cp_us, 2), "live_gflop": round(cp_gflop, 3),
               "TFLOP/s": round(cp_gflop / cp_us * 1e3, 1),
               "frac": round(cp_gflop / cp_us * 1e3 / PEAK_BF16_TFLOPS, 4)}
+
+    # ---- the other two forward workloads of the configuration list
+    # (reported beside the headline): the F5-style DiT layer (fp16, D 64,
+    # RoPE on head 0 only, row 1's last 300 keys masked) and the padded
+    # Qwen-shaped CFG pair (bf16, materialized 4-D bool mask).  Execute =
+    # K pass + attention kernel, layout planned once; attention_us: the
+    # attention kernel alone (events around back-to-back launches).
+    def time_fwd(case, gflop, peak, n=50):
+        kw = dict(scale=case.scale, rope_base=case.rope_base, pe_attn_head=case.pe_attn_head)
+        if case.mask_kind == W.MASK_BOOL:
+            kw["mask"] = case.mask.to(dev)
+        call = mz.FwdCall(case.q.to(dev), case.k.to(dev), case.v.to(dev), **kw)
+        call.plan()
+        for _ in range(5):
+            call.execute()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            call.execute()
+        e1.record()
+        torch.cuda.synchronize()
+        exe = e0.elapsed_time(e1) / n * 1e3
+        call.rotate_k()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            call.attend()
+        e1.record()
+        torch.cuda.synchronize()
+        att = e0.elapsed_time(e1) / n * 1e3
+        return {"execute_us": round(exe, 2), "attention_us": round(att, 2), "live_gflop": round(gflop, 3),
+                "TFLOP/s": round(gflop / exe * 1e3, 1), "frac": round(gflop / exe * 1e3 / peak, 4),
+                "attention_TFLOP/s": round(gflop / att * 1e3, 1),
+                "attention_frac": round(gflop / att * 1e3 / peak, 4)}
+
+    f5 = W.f5_dit_layer()
+    f5_gflop = 4 * 64 * 16 * 1500 * (1500 + 1200) / 1e9
+    other_fwd = {
+        "f5_dit_layer": {"workload": "F5-style DiT layer: B 2 (CFG), H 16, S 1500, D 64, fp16, RoPE base 1e4 on "
+                                     "head 0 only, row 1 keys 1200-1499 masked ([2,1,1,1500] bool)",
+                         **time_fwd(f5, f5_gflop, PEAK_BF16_TFLOPS)},
+        "qwen_padded": {"workload": "padded Qwen-shaped CFG pair: B 2, S 2048, Hq 16 / Hkv 8, D 128, bf16, RoPE "
+                                    "base 1e6, [2,1,2048,2048] bool mask (row 1: 800 x 800 live)",
+                        **time_fwd(W.qwen_cfg_padded(), fwd_flops() / 1e9, PEAK_BF16_TFLOPS)},
+    }
 
     # ---- the packed workload with q / k RMSNorm before RoPE (reported, not
     # the headline): execute = K pass (normalise + rotate) + attention kernel
@@ -421,7 +513,30 @@ def main(argv=None):
             sc_.execute()
         e1.record()
         torch.cuda.synchronize()
-        short.append({"seq": S, "execute_us": round(e0.elapsed_time(e1) / 100 * 1e3, 2)})
+        eager = e0.elapsed_time(e1) / 100 * 1e3
+        # the same execute recorded 20 times in one graph (GPU time without
+        # the host's launch path)
+        gs = torch.cuda.Stream()
+        gc_ = mz.FwdCall(sq, sk, sv, rope_base=1e4, stream=gs)
+        with torch.cuda.stream(gs):
+            gc_.plan()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for _ in range(20):
+                gc_.execute()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) / 200 * 1e3
+        del g
+        short.append({"seq": S, "execute_us": round(eager, 2), "graph_us": round(graph_us, 2),
+                      "launches": 1 if S <= 64 else 2})
 
     # ---- the append step (reported, not the headline): the static-cache
     # step that reads the filled length on the device, rotates q and the new
@@ -534,9 +649,12 @@ def main(argv=None):
             },
             "by_fill": by_fill,
         },
+        "other_forward": other_fwd,
         "causal_prefill": causal,
         "qk_norm": qk_norm,
-        "short_bidirectional": {"workload": "B 2 (CFG), Hq 16 / Hkv 2, D 128, bf16, RoPE base 1e4, no mask",
+        "short_bidirectional": {"workload": "B 2 (CFG), Hq 16 / Hkv 2, D 128, bf16, RoPE base 1e4, no mask; "
+                                            "execute_us: events around 100 eager executes (host launch path "
+                                            "included); graph_us: 20 executes replayed as one graph",
                                 "by_seq": short},
         "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
                                       "length on the device, RoPE base 1e4 on q and the new key",

@@ -52,7 +52,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
+def build(jobs: int = 8, verbose: bool = True) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
@@ -72,7 +72,7 @@ def build(jobs: int = 4, verbose: bool = True) -> str:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--jobs", type=int, default=8)
     a = ap.parse_args(argv)
     build(a.jobs)
     return 0

@@ -7,6 +7,9 @@
 // p_ij = exp(scale * <q_i, k_j> - max), after interleaved RoPE on q and k.
 // Non-live keys are removed by a select (their score becomes -inf before the
 // max and their weight exactly 0), never by a finite bias.
+#include <atomic>
+
+#include "fwd_mfma.h"
 #include "mz_common.h"
 #include "mz_internal.h"
 
@@ -159,15 +162,6 @@ __global__ __launch_bounds__(256) void seg_prep_kernel(const FwdParams p, int bm
 // Prepass 3: rotate the K heads that get RoPE into the workspace (once per
 // key, instead of once per query tile that visits it).
 // ---------------------------------------------------------------------------
-__device__ inline int key_position(const FwdParams& p, int b, int j) {
-  if (p.pos_k_mode == POS_ARANGE) return j;
-  return p.pos_k[b * p.pos_k_sb + j];  // user array, or derived by seg_prep_kernel
-}
-
-__device__ inline int query_position(const FwdParams& p, int b, int i) {
-  if (p.pos_q_mode == POS_ARANGE) return i;
-  return p.pos_q[b * p.pos_q_sb + i];
-}
 
 // One thread per 8 consecutive elements of a K row: 4 adjacent pairs
 // (interleaved), or with HALF 8 elements of the first half and their 8
@@ -345,696 +339,6 @@ __global__ void mask_tiles_kernel(const FwdParams p, int bm) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel, bf16 / fp16, MFMA 32x32x16.
-//
-// One work-group = (b, h, 128 queries); 4 waves of 32 queries each.  Scores
-// are computed transposed, S^T = K Q^T, so that every lane owns one query:
-// the row max and row sum need one cross-lane exchange (lanes l, l^32) and
-// the output O^T = V^T P^T is rescaled lane-locally.  P^T leaves the
-// accumulator registers directly as the B operand of the P.V MFMA; V^T comes
-// from LDS through the transposing read.
-//
-// Q is pre-multiplied by scale * log2(e) before rounding to the MFMA type,
-// so scores arrive in the log2 domain.  The running max is raised only when
-// a new score exceeds it by more than 2^8 (otherwise exponentials stay below
-// 256 and nothing is rescaled); numerator and denominator always share the
-// same reference, so the result is the same softmax.
-//
-// ---------------------------------------------------------------------------
-constexpr float LAZY_RESCALE_LOG2 = 8.0f;
-
-// LDS row layout of the K and V tiles: K rows D + 8 elements apart, V rows
-// D + 32 apart.  With 64 four-byte banks, the 16 K rows one operand fetch
-// touches (same 16-byte chunk) then start 4 banks apart, and the 4 V rows a
-// transposing read touches (64 bytes each per pair of lane groups) 16 banks
-// apart, so neither access has bank conflicts.
-template <int D> struct Lay {
-  static constexpr int KS = D + 8, VS = D + 32;
-};
-
-// Tile class bytes kept in LDS (boolean-mask mode) when the key axis has at
-// most this many tiles; longer rows read them from global memory.
-constexpr int CLS_LDS = 4096;
-
-// NSTR key streams per work-group.  With NSTR 2 the work-group has 8 waves:
-// waves w and w + 4 own the same 32 queries and take alternate live key
-// tiles (each stream with its own copies and LDS stages), and the two
-// partial results are combined through LDS at the end.  A query tile's
-// chain of dependent steps is then half as long, at the same number of
-// waves per CU, which evens out work-groups whose key ranges differ.
-template <typename T, int D, int MK, int NSTR>
-__global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const FwdParams p) {
-  static_assert(NSTR == 1 || NSTR == 2, "one or two key streams");
-  constexpr int NT = 256 * NSTR;
-  constexpr int BM = FWD_BM, BN = FWD_BN;
-  constexpr int NS = D / 16;  // k-steps of K Q^T
-  constexpr int ND = D / 32;  // 32-row d blocks of O^T
-  constexpr int CH = D / 8;   // 16-byte chunks of data per row
-  constexpr int KS = Lay<D>::KS, VS = Lay<D>::VS;
-  constexpr int KCH = KS / 8, VCH = VS / 8;  // 16-byte slots per padded row
-  // one direct-to-LDS wave instruction fills 64 consecutive slots (1 KB);
-  // a padded tile of 64 rows takes KCH (VCH) of them
-  constexpr int KINS = KCH, VINS = VCH;
-  constexpr int KPW = (KINS + 3) / 4, VPW = (VINS + 3) / 4;  // per wave, at most
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTR][2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTR][2][BN * VS];
-  __shared__ uint8_t cls_lds[MK == 1 ? CLS_LDS : 1];
-  __shared__ int n_live_lds;
-
-  // work order: (kv-head, b, query tile, head within the group).  The G
-  // heads that share K/V run side by side and long tiles start first; the
-  // contiguous range each XCD receives covers whole kv-heads, so their K/V
-  // stay in that XCD's L2, and batches mix within every XCD.
-  const int nwork = p.B * p.Hq * p.n_qt;
-  const int w = xcd_remap(blockIdx.x, nwork);
-  const int g = w % p.G;
-  // causal: the last query tiles have the most keys, so they start first
-  const int qt = MK == 3 ? p.n_qt - 1 - (w / p.G) % p.n_qt : (w / p.G) % p.n_qt;
-  const int kvb = w / (p.G * p.n_qt);
-  const int b = kvb % p.B, hk = kvb / p.B;
-  const int h = hk * p.G + g;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = (tid >> 6) & 3;  // query strip
-  const int str = NSTR == 1 ? 0 : tid >> 8;  // key stream
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int qi = qt * BM + wave * 32 + l32;
-  const bool qvalid = qi < p.Sq;
-
-  // ---- Q fragment, pre-scaled: B operand of S^T = K Q^T.  Its loads (q,
-  // the norm weights, the cos / sin table entries) are issued here; the
-  // arithmetic (finish_q) runs once the first K / V tile copies are
-  // issued, so the two latencies overlap.
-  uint4 qf[NS];
-  const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
-  const bool rot = h < p.n_rot;
-  const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
-  const float qsc = p.scale_log2;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = qvalid ? *(const uint4*)(qrow + s * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
-  // RMSNorm of q: this lane holds half of the row (elements s*16 + hh*8
-  // + e), lane ^ 32 the other half
-  const bool qnorm = p.q_norm_w != nullptr;
-  uint4 wq[NS];
-  if (qnorm) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) wq[s] = *(const uint4*)((const uint16_t*)p.q_norm_w + s * 16 + hh * 8);
-  }
-  // cos / sin of this lane's pairs at the query's position, read from the
-  // table as 16-byte vectors, all issued before any is used: interleaved,
-  // piece s holds pairs s*8 + hh*4 + t (t < 4), slot 4s + t; half split,
-  // piece s < NS/2 holds pairs s*16 + hh*8 + j (j < 8), slot 8s + j; slot
-  // m is half of tb[m / 2].  A position past the table (rare) takes the
-  // direct formula instead (same bits), a branch at the use.
-  const bool in_tab = qpos >= 0 && qpos < p.rope_tab_len;
-  float4 tb[2 * NS];
-  if (qvalid && rot) {
-    const float2* trow = p.rope_tab + (size_t)(in_tab ? qpos : 0) * (D / 2);
-    if (p.rope_style == 1) {
-#pragma unroll
-      for (int s = 0; s < NS / 2; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tb[4 * s + j] = ((const float4*)(trow + s * 16 + hh * 8))[j];
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) tb[2 * s + j] = ((const float4*)(trow + s * 8 + hh * 4))[j];
-    }
-  }
-  auto finish_q = [&]() {
-    float qinv = 1.f;
-    if (qnorm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float a = Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), c = Elem<T>::to_f32((uint16_t)(wv[t] >> 16));
-          ss = fmaf(a, a, fmaf(c, c, ss));
-        }
-      }
-      qinv = rsqrtf(half_swap_sum(ss) / (float)D + p.norm_eps);
-    }
-    // element e (0..7) of piece s, normalised when q_norm_w is set
-    auto qn = [&](float x, int s, int e) __attribute__((always_inline)) -> float {
-      if (!qnorm) return x;
-      const uint32_t w2 = e < 4 ? (e < 2 ? wq[s].x : wq[s].y) : (e < 6 ? wq[s].z : wq[s].w);
-      return x * qinv * Elem<T>::to_f32((uint16_t)(w2 >> (16 * (e & 1))));
-    };
-    auto cs_at = [&](int m, int pair) -> float2 {
-      const float4 v = tb[m >> 1];
-      float2 cs = (m & 1) ? make_float2(v.z, v.w) : make_float2(v.x, v.y);
-      if (__builtin_expect(!in_tab, 0)) cs = rope_cs_direct(qpos, pair, D, p.rs);
-      return cs;
-    };
-    if (qvalid && rot && p.rope_style == 1) {
-      // half split: element e of chunk s pairs with element e of chunk
-      // s + NS/2 (d and d + D/2), both held by this lane
-#pragma unroll
-      for (int s = 0; s < NS / 2; ++s) {
-        uint32_t lo[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
-        uint32_t hi[4] = {qf[s + NS / 2].x, qf[s + NS / 2].y, qf[s + NS / 2].z, qf[s + NS / 2].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float r[2][2];  // [first half, second half][element 2t, 2t + 1]
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float a = qn(Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e))), s, 2 * t + e);
-            const float c = qn(Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e))), s + NS / 2, 2 * t + e);
-            const float2 cs = cs_at(8 * s + 2 * t + e, s * 16 + hh * 8 + 2 * t + e);
-            r[0][e] = fmaf(a, cs.x, -c * cs.y);
-            r[1][e] = fmaf(c, cs.x, a * cs.y);
-          }
-          lo[t] = Elem<T>::pack2(r[0][0] * qsc, r[0][1] * qsc);
-          hi[t] = Elem<T>::pack2(r[1][0] * qsc, r[1][1] * qsc);
-        }
-        qf[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        qf[s + NS / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      }
-    } else if (qvalid) {
-      // interleaved: the pairs are the two halves of each 32-bit word
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
-        const int d0 = s * 16 + hh * 8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float a = qn(Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), s, 2 * t);
-          float c = qn(Elem<T>::to_f32((uint16_t)(wv[t] >> 16)), s, 2 * t + 1);
-          if (rot) {
-            const float2 cs = cs_at(4 * s + t, d0 / 2 + t);
-            const float ra = fmaf(a, cs.x, -c * cs.y);
-            const float rc = fmaf(c, cs.x, a * cs.y);
-            a = ra;
-            c = rc;
-          }
-          wv[t] = Elem<T>::pack2(a * qsc, c * qsc);
-        }
-        qf[s] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
-    }
-  };
-
-  // ---- K / V sources
-  const uint16_t* kbase;
-  int64_t kstride;
-  if (hk < p.n_rot_kv) {
-    kbase = (const uint16_t*)p.k_rot + ((int64_t)(b * p.n_rot_kv + hk) * p.Sk) * D;
-    kstride = D;
-  } else {
-    kbase = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1];
-    kstride = p.ks[2];
-  }
-  const uint16_t* vbase = (const uint16_t*)p.v + b * p.vs[0] + hk * p.vs[1];
-  const int64_t vstride = p.vs[2];
-
-  // ---- which key tiles to visit
-  int kt_beg = 0, kt_end = p.n_kt, full_beg = 0, full_end = 0;
-  int lo = 0, hi = p.Sk;
-  const uint8_t* cls_row = nullptr;
-  const uint64_t* brow = nullptr;  // this lane's key-bit words (valid queries)
-  bool cls_in_lds = false;
-  if constexpr (MK == 2) {
-    const int4 r = p.qt_range[(int64_t)b * p.n_qt + qt];
-    kt_beg = r.x; kt_end = r.y; full_beg = r.z; full_end = r.w;
-    if (qvalid) {
-      const int2 qr = p.q_range[(int64_t)b * p.Sq + qi];
-      lo = qr.x; hi = qr.y;
-    } else {
-      lo = 0; hi = 0;
-    }
-  } else if constexpr (MK == 3) {
-    // causal: keys [0, i] of query i; whole tiles below the tile's first
-    // query need no per-element test
-    const int q_first = qt * BM, q_last = min(p.Sq, q_first + BM) - 1;
-    kt_end = (min(p.Sk, q_last + 1) + BN - 1) / BN;
-    full_end = min(p.Sk, q_first + 1) / BN;
-    lo = 0;
-    hi = qvalid ? min(p.Sk, qi + 1) : 0;
-  } else if constexpr (MK == 1) {
-    const int bm_ = p.Bm == 1 ? 0 : b, hm_ = p.Hm == 1 ? 0 : h;
-    cls_row = p.tile_cls + ((int64_t)(bm_ * p.Hm + hm_) * p.n_qt + qt) * p.n_kt;
-    if (qvalid)
-      brow = p.mask_bits + ((int64_t)(bm_ * p.Hm + hm_) * p.mask_rows + (p.ms[2] == 0 ? 0 : qi)) * p.n_kt;
-    cls_in_lds = p.n_kt <= CLS_LDS;
-    if (cls_in_lds) {
-      for (int i = tid; i < p.n_kt; i += NT) cls_lds[i] = cls_row[i];
-      if (NSTR == 2 && tid == 0) n_live_lds = 0;
-      __syncthreads();
-    } else if (NSTR == 2) {
-      if (tid == 0) n_live_lds = 0;
-      __syncthreads();
-    }
-  }
-  auto cls_at = [&](int kt) -> int {
-    if constexpr (MK == 1) return cls_in_lds ? cls_lds[kt] : cls_row[kt];
-    return 1;
-  };
-  auto next_live = [&](int kt) {
-    if constexpr (MK == 1) {
-      while (kt < kt_end && cls_at(kt) == 0) ++kt;
-    }
-    return kt;
-  };
-  const int first_tail_tile = p.Sk / BN;  // tiles from here on reach past Sk
-  // live key tiles of the query tile; with two streams their count fixes how
-  // many barriers each stream passes (the read is after the prologue barrier)
-  int n_live = kt_end > kt_beg ? kt_end - kt_beg : 0;
-  if constexpr (MK == 1 && NSTR == 2) {
-    int c = 0;
-    for (int i = tid; i < p.n_kt; i += NT) c += cls_at(i) != 0;
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-    if (lane == 0 && c != 0) atomicAdd(&n_live_lds, c);
-  }
-
-  // ---- direct-to-LDS tile loads.  Slot q of a padded tile is row q / KCH,
-  // chunk q % KCH; pad slots (chunk >= CH) load chunk 0 of their row again.
-  // The per-lane byte offsets from the tile's first row are fixed (row
-  // strides are below 2^24 elements, so a 64-row tile spans less than 2^31
-  // bytes); only the last tile, whose rows past Sk load row Sk - 1 instead
-  // (their keys are masked), needs them recomputed.
-  uint32_t koff[KPW], voff[VPW];
-  auto slot_off = [&](int ins, int nch, int64_t stride) -> uint32_t {
-    const int q = ins * 64 + lane;
-    const int row = q / nch;
-    const int ch = q % nch;
-    return (uint32_t)((row * stride + (ch < CH ? ch : 0) * 8) * 2);
-  };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-#pragma unroll
-  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride);
-#pragma unroll
-  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave_u, VCH, vstride);
-  const uint32_t ks_lds = lds_addr(&Ks[str][0][0]), vs_lds = lds_addr(&Vs[str][0][0]);
-  // descriptor of one K or V tile: its rows below Sk only, so rows past Sk
-  // read as zeros (their keys are masked)
-  auto tile_desc = [&](const uint16_t* base, int64_t stride, int kt) -> u32x4_t {
-    const int key0 = kt * BN;
-    const int rows = min(BN, p.Sk - key0);
-    return buf_desc(base + (int64_t)key0 * stride, (uint32_t)(((int64_t)(rows - 1) * stride + D) * 2));
-  };
-  auto load_k = [&](int kt, int stage) {
-    const u32x4_t d = tile_desc(kbase, kstride, kt);
-    const uint32_t kdst = ks_lds + stage * (BN * KS * 2);
-#pragma unroll
-    for (int u = 0; u < KPW; ++u)
-      if (u * 4 + wave_u < KINS) lds_dma16_b(d, koff[u], kdst + (u * 4 + wave_u) * 1024);
-  };
-  auto load_v = [&](int kt, int stage) {
-    const u32x4_t d = tile_desc(vbase, vstride, kt);
-    const uint32_t vdst = vs_lds + stage * (BN * VS * 2);
-#pragma unroll
-    for (int u = 0; u < VPW; ++u)
-      if (u * 4 + wave_u < VINS) lds_dma16_b(d, voff[u], vdst + (u * 4 + wave_u) * 1024);
-  };
-  // the copies of one step spread over its MFMA slots: slot u < KPW is K
-  // copy instruction u of this wave, slot KPW + u V copy u
-  struct DmaPlan {
-    u32x4_t dk, dv;
-    uint32_t kdst, vdst;
-    bool k_on, v_on;
-  };
-  auto dma_slot = [&](const DmaPlan& pl, int slot) {
-    if (slot < KPW) {
-      if (pl.k_on && slot * 4 + wave_u < KINS) lds_dma16_b(pl.dk, koff[slot], pl.kdst + (slot * 4 + wave_u) * 1024);
-    } else {
-      const int u = slot - KPW;
-      if (pl.v_on && u * 4 + wave_u < VINS) lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
-    }
-  };
-
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t oacc[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-  const int grp = lane >> 4, gi = lane & 15, rr = gi >> 2, cc = gi & 3;
-
-  const f32x16_t zero16 = {};
-  // scores of two consecutive tiles; the steady-state loop is unrolled by
-  // two so that the arrays swap roles instead of being copied
-  f32x16_t sA[2], sB[2];
-  float mu = 0.f;  // reference of the exponentials (m, or 0 before any live key)
-  // CINIT (D 64): the K Q^T accumulators start from -mu in every element, so
-  // scores arrive relative to the reference and the exponentials need no
-  // subtraction.  At D 128 the 16 extra registers would spill; there the
-  // accumulators start from zero and mu is subtracted before each exponential.
-  constexpr bool CINIT = D == 64;
-  f32x16_t cinit = {};
-
-  // S^T = K Q^T + cinit of one tile, plain (prologue)
-  auto qk = [&](int stage, f32x16_t (&sacc)[2]) {
-    const uint16_t* kt_lds = &Ks[str][stage][0];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 a = *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * s + hh) * 8];
-        sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? (CINIT ? cinit : zero16) : sacc[kb]);
-      }
-    }
-  };
-  // non-live keys of a boundary tile -> -inf.  Key kb*32 + c + hh*4 of the
-  // tile (c a compile-time constant per register) is compared through
-  // per-tile thresholds, so no per-register key offset stays in registers.
-  auto mask_tile = [&](int kt, f32x16_t (&sc)[2]) {
-    bool check;
-    if constexpr (MK == 2 || MK == 3) check = !(kt >= full_beg && kt < full_end);
-    else if constexpr (MK == 1) check = cls_at(kt) == 2 || kt >= first_tail_tile;
-    else check = kt >= first_tail_tile;
-    if (__builtin_expect(check, 0)) {
-      // kept a branch (boundary tiles are few): without the barrier to
-      // speculation the compiler turns this into selects on every tile
-      __asm__ volatile("");
-      const int base = kt * BN + hh * 4;
-      const int lim = p.Sk - base;       // keys past Sk
-      const int lo_t = lo - base, hi_t = hi - base;
-      // the lane's key bits of this tile, shifted to its half (keys past Sk
-      // carry 0 bits); lanes without a query see none live
-      uint64_t kbits = 0;
-      if constexpr (MK == 1) {
-        if (brow != nullptr) kbits = brow[kt] >> (hh * 4);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = kb * 32 + (v >> 2) * 8 + (v & 3);
-          bool live;
-          if constexpr (MK == 2 || MK == 3) live = c >= lo_t && c < hi_t;
-          else if constexpr (MK == 1) live = (kbits >> c) & 1;
-          else live = c < lim;
-          sc[kb][v] = live ? sc[kb][v] : -INFINITY;
-        }
-      }
-    }
-  };
-  auto rowmax = [&](const f32x16_t (&sc)[2]) -> float {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, sc[kb][v]), sc[kb][v + 1]);
-    return half_swap_max(mx);
-  };
-
-  // Software pipeline over the live key tiles t(0), t(1), ...  During step
-  // j, K of t(j+1) and V of t(j) are resident (K one tile ahead of V) while
-  // K of t(j+2) and V of t(j+1) stream in; one barrier per step.  LDS
-  // operands are read PF MFMAs ahead of their use; a scheduling fence after
-  // each MFMA keeps the planned order.
-  constexpr int PF = 2;
-  uint4 pk[2][2];
-  constexpr int NSLOT = KPW + VPW;  // copy instructions per wave and step, at most
-  // P.V of one whole tile, P from pk
-  auto pv_all = [&](int vstage) {
-    const uint16_t* vt_lds = &Vs[str][vstage][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
-          const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
-          const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
-          const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
-          oacc[db] = mfma32<T>(make_uint4(a0.x, a0.y, a1.x, a1.y), pk[kb][jj], oacc[db]);
-        }
-      }
-    }
-  };
-  // the last tile: its exponentials, then its P.V
-  auto last_tile = [&](int vstage, f32x16_t (&scur)[2]) {
-    float lsa = 0.f, lsb = 0.f;
-    uint32_t wv[2][2][4];
-    static_for<16>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
-      const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - (CINIT ? 0.f : mu));
-      const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - (CINIT ? 0.f : mu));
-      wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
-      if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
-      else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
-      if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
-    });
-    l_run += lsa + lsb;
-    pv_all(vstage);
-  };
-
-  // One exponential piece: 2 of the 32 scores of a lane (tile t(j)), packed
-  // into P block (kb, jj) and added to the row sum.
-  constexpr int NQK = 2 * NS, NPV = 4 * ND;
-  static_assert(16 % NQK == 0, "exponential pieces spread evenly over the K Q^T MFMAs");
-  static_assert(NSLOT <= NPV, "every copy has a P.V slot");
-  auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4], f32x16_t (&scur)[2]) {
-    constexpr int h = decltype(hc)::value;
-    constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
-    const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - (CINIT ? 0.f : mu));
-    const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - (CINIT ? 0.f : mu));
-    wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
-    __asm__ volatile("" ::"v"(wv[kb][jj][e]));
-    if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
-    else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
-    if constexpr (e == 3) pk[kb][jj] = make_uint4(wv[kb][jj][0], wv[kb][jj][1], wv[kb][jj][2], wv[kb][jj][3]);
-  };
-
-  float mx = -INFINITY;  // row max of the newest scores
-  // Steady-state step, split: the 2*NS K Q^T MFMAs of t(j+1) come first,
-  // one exponential piece of t(j) after each (P block (kb, jj) is complete
-  // before the P.V half starts); then the 4*ND P.V MFMAs of t(j) with the
-  // copies of the step and, once the K Q^T results have landed, the mask and
-  // row max of t(j+1) (after the half for boolean masks), so that the next
-  // step does not wait on them.
-  auto step_split = [&](int kstage, int vstage, const DmaPlan& pl, f32x16_t (&scur)[2], f32x16_t (&snext)[2],
-                        int kt_next) {
-    const uint16_t* kt_lds = &Ks[str][kstage][0];
-    const uint16_t* vt_lds = &Vs[str][vstage][0];
-    float lsa = 0.f, lsb = 0.f;
-    uint32_t wv[2][2][4];
-    auto kfrag = [&](auto gc) -> uint4 {
-      constexpr int g = decltype(gc)::value, ss = g >> 1, kb = g & 1;
-      return *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * ss + hh) * 8];
-    };
-    auto vfrag = [&](auto gc) -> uint4 {
-      constexpr int g = decltype(gc)::value, kb = g / (2 * ND), jj = (g / ND) & 1, db = g % ND;
-      const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
-      const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
-      const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
-      const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
-      return make_uint4(a0.x, a0.y, a1.x, a1.y);
-    };
-    uint4 frk[PF], frv[PF];
-    static_for<PF>([&](auto gc) { frk[decltype(gc)::value] = kfrag(gc); });
-    static_for<NQK>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, ss = i >> 1, kb = i & 1;
-      const uint4 f = frk[i % PF];
-      if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
-      else frv[i + PF - NQK] = vfrag(std::integral_constant<int, i + PF - NQK>{});
-      snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? (CINIT ? cinit : zero16) : snext[kb]);
-      static_for<16 / NQK>([&](auto pc) { exp_piece(std::integral_constant<int, i * (16 / NQK) + decltype(pc)::value>{}, lsa, lsb, wv, scur); });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    static_for<NPV>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
-      const uint4 f = frv[i % PF];
-      if constexpr (i + PF < NPV) frv[i % PF] = vfrag(std::integral_constant<int, i + PF>{});
-      oacc[db] = mfma32<T>(f, pk[kb][jj], oacc[db]);
-      if constexpr (i < NSLOT) dma_slot(pl, i);
-      if constexpr (i == 3 && MK != 1) {
-        mask_tile(kt_next, snext);
-        mx = rowmax(snext);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    // boolean masks: a mixed tile loads its key bits, a wait that would
-    // also cover the copies just issued, so it comes after the P.V half
-    if constexpr (MK == 1) {
-      mask_tile(kt_next, snext);
-      mx = rowmax(snext);
-    }
-    l_run += lsa + lsb;
-  };
-
-  // this stream's live tiles: every NSTR-th one, starting at its index
-  auto advance = [&](int k) {
-    k = next_live(k + 1);
-    if constexpr (NSTR == 2) {
-      if (k < kt_end) k = next_live(k + 1);
-    }
-    return k;
-  };
-  int kt = next_live(kt_beg);
-  if (NSTR == 2 && str == 1 && kt < kt_end) kt = next_live(kt + 1);
-  int kn = kt < kt_end ? advance(kt) : kt_end;
-  if (kt < kt_end) {
-    load_k(kt, 0);
-    load_v(kt, 0);
-  }
-  if (kn < kt_end) load_k(kn, 1);
-  finish_q();
-  // every prologue load completes here (the first tile copies are in flight
-  // meanwhile), so that no wait for one is left inside the tile loop, where
-  // it would also wait for the tile copies
-#pragma unroll
-  for (int s = 0; s < NS; ++s) __asm__ volatile("" ::"v"(qf[s].x), "v"(qf[s].y), "v"(qf[s].z), "v"(qf[s].w));
-  __asm__ volatile("" ::"v"(lo), "v"(hi));
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  auto rescale_step = [&](f32x16_t (&sc)[2]) {
-    // ---- online softmax with lazy rescaling.  The reference m of a query
-    // moves only when a score exceeds it by more than 2^8 (otherwise the
-    // exponentials stay below 256); numerator and denominator always share
-    // it, so the result is the same softmax.  With CINIT, scores and mx are
-    // relative to the current reference mu, and a move shifts the scores of
-    // the tile at hand and the start value of the next ones.
-    const float mx_abs = CINIT ? mu + mx : mx;
-    const bool need = m_run == -INFINITY ? mx > -INFINITY : mx_abs > m_run + LAZY_RESCALE_LOG2;
-    if (__any(need)) {
-      const float m_new = need ? mx_abs : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      const float mu_new = m_new == -INFINITY ? 0.f : m_new;
-      const float shift = mu - mu_new;
-      m_run = m_new;
-      mu = mu_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-      if constexpr (CINIT) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sc[kb][v] += shift;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cinit[v] = -mu;
-      }
-    }
-  };
-  auto step_top = [&](int j) {
-    // K of t(j+1) and V of t(j) have landed once this barrier passes, and
-    // every wave is done with the stages the next copies overwrite
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-  int j = 0;
-  // copies of one step: K of t(j+2) and V of t(j+1)
-  auto plan_step = [&](int kn2) {
-    DmaPlan pl;
-    pl.k_on = kn2 < kt_end;
-    pl.dk = tile_desc(kbase, kstride, pl.k_on ? kn2 : kn);
-    pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
-    pl.v_on = true;
-    pl.dv = tile_desc(vbase, vstride, kn);
-    pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
-    return pl;
-  };
-  // one steady-state step: tile t(j) scores in sc, t(j+1) scores into sn
-  auto steady = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    step_top(j);
-    const int kn2 = advance(kn);
-    // K of t(j+2) and V of t(j+1), issued between the MFMAs of this step
-    const DmaPlan pl = plan_step(kn2);
-    rescale_step(sc);
-    step_split((j + 1) & 1, j & 1, pl, sc, sn, kn);
-    kt = kn;
-    kn = kn2;
-    ++j;
-  };
-  if (kt < kt_end) {
-    qk(0, sA);
-    mask_tile(kt, sA);
-    mx = rowmax(sA);
-    bool in_b = false;  // the current tile's scores are in sB
-    while (kn < kt_end) {
-      steady(sA, sB);
-      if (kn >= kt_end) {
-        in_b = true;
-        break;
-      }
-      steady(sB, sA);
-    }
-    // the last tile
-    step_top(j);
-    if (in_b) {
-      rescale_step(sB);
-      last_tile(j & 1, sB);
-    } else {
-      rescale_step(sA);
-      last_tile(j & 1, sA);
-    }
-  }
-
-  if constexpr (NSTR == 2) {
-    // a stream passes one barrier per live tile it takes (plus the prologue
-    // one), so stream 1 passes one fewer when the count is odd
-    if constexpr (MK == 1) n_live = n_live_lds;  // counted before the prologue barrier
-    if (str == 1 && (n_live & 1)) __syncthreads();
-    // every copy and every LDS operand read of both streams is complete:
-    // stream 1 parks (m, l, O^T) in the K stages, lane-major so that each
-    // access is a conflict-free 16-byte one, and stream 0 folds it in
-    static_assert(sizeof(float) * (4 * ND * 16 * 64 + 2 * 4 * 64) <= sizeof(Ks), "partials fit the K stages");
-    float* part = reinterpret_cast<float*>(&Ks[0][0][0]);
-    float2* part_ml = reinterpret_cast<float2*>(part + 4 * ND * 16 * 64);
-    if (str == 1) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4)
-          *(float4*)&part[((wave * ND + db) * 4 + v4) * 256 + lane * 4] =
-              make_float4(oacc[db][v4 * 4], oacc[db][v4 * 4 + 1], oacc[db][v4 * 4 + 2], oacc[db][v4 * 4 + 3]);
-      part_ml[wave * 64 + lane] = make_float2(m_run, l_run);
-    }
-    __syncthreads();
-    if (str == 1) return;
-    // both partials are relative to their own reference (m, or nothing
-    // accumulated when m = -inf); rebase both to the larger one
-    const float2 mlb = part_ml[wave * 64 + lane];
-    const float m_new = fmaxf(m_run, mlb.x);
-    const float fa = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-    const float fb = mlb.x == -INFINITY ? 0.f : fast_exp2(mlb.x - m_new);
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const float4 y = *(const float4*)&part[((wave * ND + db) * 4 + v4) * 256 + lane * 4];
-        oacc[db][v4 * 4 + 0] = oacc[db][v4 * 4 + 0] * fa + y.x * fb;
-        oacc[db][v4 * 4 + 1] = oacc[db][v4 * 4 + 1] * fa + y.y * fb;
-        oacc[db][v4 * 4 + 2] = oacc[db][v4 * 4 + 2] * fa + y.z * fb;
-        oacc[db][v4 * 4 + 3] = oacc[db][v4 * 4 + 3] * fa + y.w * fb;
-      }
-    l_run = l_run * fa + mlb.y * fb;
-    m_run = m_new;
-  }
-
-  // ---- epilogue: O = O^T / l, lse
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qvalid) {
-    uint16_t* orow = (uint16_t*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)qi * p.os[2];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + g4 * 8 + hh * 4;
-        uint2 st;
-        st.x = Elem<T>::pack2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
-        st.y = Elem<T>::pack2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
-        *(uint2*)(orow + d) = st;
-      }
-    }
-    if (p.lse != nullptr && hh == 0)
-      p.lse[((int64_t)b * p.Hq + h) * p.Sq + qi] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // fp32 kernel: one wave per 64 queries, one lane per query, fp32 FMA.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -1197,10 +501,21 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows of at most KR_MAX_TILES key tiles (16-bit types) rotate their K in
+// the attention kernel: no K pass, one launch per execute.  The rotated
+// keys must then have the default positions 0 .. Sk-1 (inside the cos /
+// sin table, which covers max(Sq, Sk) positions); explicit or
+// segment-derived key positions take the K pass.
+constexpr int KR_MAX_TILES = 1;
+static bool k_in_attention(const FwdParams& p) {
+  if (p.dtype == 0 || p.n_rot_kv == 0 || p.n_kt > KR_MAX_TILES) return false;
+  return p.n_rotk == 0 || (p.pos_k_mode == POS_ARANGE && p.Sk <= p.rope_tab_len);
+}
+
 // K heads that get RoPE, rotated into the workspace (reads the table and the
 // derived key positions written by the plan).
 hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
-  if (p.n_rot_kv > 0 && p.Sk > 0 && p.B > 0) {
+  if (p.n_rot_kv > 0 && p.Sk > 0 && p.B > 0 && !k_in_attention(p)) {
     if (p.dtype == 0) {
       const int rows_per_blk = 256 / (p.D / 2);
       const unsigned nx = (unsigned)((p.Sk + rows_per_blk - 1) / rows_per_blk);
@@ -1221,26 +536,6 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int NSTR>
-static void launch_mfma_n(const FwdParams& p, unsigned nwork, hipStream_t s) {
-  const dim3 blk(256 * NSTR);
-  if (p.mask_kind == 3) fwd_mfma_kernel<T, D, 3, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
-  else if (p.mask_kind == 2) fwd_mfma_kernel<T, D, 2, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
-  else if (p.mask_kind == 1) fwd_mfma_kernel<T, D, 1, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
-  else fwd_mfma_kernel<T, D, 0, NSTR><<<dim3(nwork), blk, 0, s>>>(p);
-}
-
-template <typename T>
-static void launch_mfma(const FwdParams& p, unsigned nwork, int nstr, hipStream_t s) {
-  if (p.D == 64) {
-    if (nstr == 2) launch_mfma_n<T, 64, 2>(p, nwork, s);
-    else launch_mfma_n<T, 64, 1>(p, nwork, s);
-  } else {
-    if (nstr == 2) launch_mfma_n<T, 128, 2>(p, nwork, s);
-    else launch_mfma_n<T, 128, 1>(p, nwork, s);
-  }
-}
-
 // Key streams per work-group.  Two when there are no more work-groups than
 // CUs and the rows are long: each CU then holds one query tile, the
 // one-stream kernel would run a single wave per SIMD, and splitting the keys
@@ -1252,16 +547,27 @@ static void launch_mfma(const FwdParams& p, unsigned nwork, int nstr, hipStream_
 // kernel already places two per CU.  MZATTN_KEY_STREAMS=1|2 overrides the
 // choice.
 constexpr int KEY_STREAMS_MIN_TILES = 24;
+// Compute units of the current device, queried once per device.
+static int cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 static int key_streams(unsigned nwork, int n_kt) {
   if (const char* e = getenv("MZATTN_KEY_STREAMS")) {
     if (e[0] == '1' && e[1] == 0) return 1;
     if (e[0] == '2' && e[1] == 0) return 2;
   }
   if (n_kt < KEY_STREAMS_MIN_TILES) return 1;
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 256;
-  return (int64_t)nwork <= (int64_t)ncu ? 2 : 1;
+  return (int64_t)nwork <= (int64_t)cu_count() ? 2 : 1;
 }
 
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
@@ -1270,10 +576,16 @@ hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
   if (f32) {
     if (p.D == 64) fwd_f32_kernel<64><<<dim3(nwork), dim3(64), 0, s>>>(p);
     else fwd_f32_kernel<128><<<dim3(nwork), dim3(64), 0, s>>>(p);
-  } else if (p.dtype == 2) {
-    launch_mfma<BF16>(p, nwork, key_streams(nwork, p.n_kt), s);
   } else {
-    launch_mfma<F16>(p, nwork, key_streams(nwork, p.n_kt), s);
+    const bool kr = k_in_attention(p);
+    const int nstr = kr ? 1 : key_streams(nwork, p.n_kt);
+    if (p.dtype == 2) {
+      if (p.D == 64) launch_mfma_bf16_d64(p, nwork, nstr, kr, s);
+      else launch_mfma_bf16_d128(p, nwork, nstr, kr, s);
+    } else {
+      if (p.D == 64) launch_mfma_f16_d64(p, nwork, nstr, kr, s);
+      else launch_mfma_f16_d128(p, nwork, nstr, kr, s);
+    }
   }
   return hipGetLastError();
 }

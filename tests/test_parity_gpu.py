@@ -771,3 +771,104 @@ def test_qk_rms_norm(cfg):
                              q_norm_w=None if wq is None else W.to_bits(wq),
                              k_norm_w=None if wk is None else W.to_bits(wk), norm_eps=1e-6)
     assert_parity(dtype, o, ref, f"rms norm {cfg}")
+
+
+# --------------------------------------------------------------------------
+# short rows: one launch per execute (K rotated in the attention kernel)
+# --------------------------------------------------------------------------
+
+SHORT_CFGS = [
+    # dtype, B, Hq, Hkv, S, D, kind, style, norms, pe_attn_head
+    ("bf16", 2, 16, 2, 16, 128, W.MASK_NONE, "interleaved", "", -1),
+    ("bf16", 2, 16, 2, 64, 128, W.MASK_NONE, "half", "", -1),
+    ("f16", 2, 4, 4, 33, 64, W.MASK_BOOL, "interleaved", "", 1),      # RoPE on head 0 only
+    ("bf16", 1, 8, 2, 50, 128, W.MASK_SEGMENT, "interleaved", "qk", -1),
+    ("f16", 2, 8, 1, 64, 64, W.MASK_CAUSAL, "half", "k", -1),
+    ("bf16", 3, 2, 2, 1, 128, W.MASK_BOOL, "half", "q", -1),
+    ("bf16", 2, 4, 4, 40, 128, W.MASK_NONE, "interleaved", "k", 0),   # no RoPE, k normalised
+]
+
+
+def _short_case(cfg):
+    dtype, B, Hq, Hkv, S, D, kind, style, norms, pe = cfg
+    seed = zlib.crc32(repr(("short",) + cfg).encode()) % 10000
+    case = W.random_fwd(seed, B, Hq, Hkv, S, S, D, dtype, kind, rope_base=1e4, pe_attn_head=pe, mask_shape="key",
+                        n_segments=2)
+    case.rope_style = style
+    cast = W.DTYPES[dtype]
+    gen = torch.Generator().manual_seed(seed + 1)
+    wq = (1.0 + 0.5 * torch.randn(D, generator=gen)).to(cast) if "q" in norms else None
+    wk = (1.0 + 0.5 * torch.randn(D, generator=gen)).to(cast) if "k" in norms else None
+    return case, wq, wk
+
+
+def _run_short(case, wq, wk, pos_k=None):
+    import masked_bidirectional_attention_amd as mz
+    kw = dict(rope_base=case.rope_base, pe_attn_head=case.pe_attn_head, rope_style=case.rope_style,
+              q_norm_weight=dev(wq), k_norm_weight=dev(wk), pos_k=dev(pos_k))
+    if case.mask_kind == W.MASK_BOOL:
+        kw["mask"] = dev(case.mask)
+    elif case.mask_kind == W.MASK_SEGMENT:
+        kw["seg_q"], kw["seg_k"] = dev(case.seg_q), dev(case.seg_k)
+    elif case.mask_kind == W.MASK_CAUSAL:
+        kw["causal"] = True
+    o = mz.mzattn_fwd(dev(case.q), dev(case.k), dev(case.v), **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("cfg", SHORT_CFGS, ids=lambda c: "-".join(map(str, c)))
+def test_short_rows_one_launch(cfg):
+    """Rows of one key tile: the K heads are normalised and rotated in the
+    attention kernel (no K pass).  Parity with the oracle, and the same bits
+    as the K-pass path, which an explicit key position array (here the
+    default positions written out) selects."""
+    case, wq, wk = _short_case(cfg)
+    o = _run_short(case, wq, wk)
+    ref, _ = mzref.mzref_fwd(case.dtype, W.to_bits(case.q), W.to_bits(case.k), W.to_bits(case.v),
+                             rope_base=case.rope_base, pe_attn_head=case.pe_attn_head, rope_style=case.rope_style,
+                             mask_kind=case.mask_kind, mask=None if case.mask is None else case.mask.numpy(),
+                             seg_q=None if case.seg_q is None else case.seg_q.numpy(),
+                             seg_k=None if case.seg_k is None else case.seg_k.numpy(),
+                             q_norm_w=None if wq is None else W.to_bits(wq),
+                             k_norm_w=None if wk is None else W.to_bits(wk))
+    assert_parity(case.dtype, o, ref, f"short {cfg}")
+    if case.mask_kind != W.MASK_SEGMENT:   # (segment positions restart: not the default arange)
+        B, S = case.q.shape[0], case.k.shape[2]
+        pos_k = torch.arange(S, dtype=torch.int32)[None].repeat(B, 1)
+        o_pass = _run_short(case, wq, wk, pos_k=pos_k)
+        assert torch.equal(o, o_pass), "one-launch path differs from the K-pass path"
+
+
+@pytest.mark.parametrize("S", [16, 64, 200])
+def test_fwd_graph_replay(S):
+    """FwdCall.execute recorded once in a HIP graph (plan outside) and
+    replayed with new inputs written in place between replays (eager work
+    in between): every replay equals an eager call on the same inputs, bit
+    for bit.  16 and 64 tokens take the one-launch path, 200 the K pass."""
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, D = 2, 16, 2, 128
+    s = torch.cuda.Stream()
+    cases = [W.random_fwd(900 + S + i, B, Hq, Hkv, S, S, D, "bf16", W.MASK_NONE, rope_base=1e4) for i in range(3)]
+    q, k, v = dev(cases[0].q), dev(cases[0].k), dev(cases[0].v)
+    call = mz.FwdCall(q, k, v, rope_base=1e4, stream=s)
+    with torch.cuda.stream(s):
+        call.plan()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call.execute()
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        q.copy_(dev(c.q))
+        k.copy_(dev(c.k))
+        v.copy_(dev(c.v))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_graph = call.out.clone()
+        o_eager = run_fwd(c)
+        assert torch.equal(o_graph, o_eager), f"replay {i}"
+        if i == 0:
+            ref, _ = oracle_fwd(c)
+            assert_parity("bf16", o_graph, ref, f"graph replay S={S}")
