@@ -342,11 +342,20 @@ def main(argv=None):
     att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
     exe_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / a.steps
     dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
-    print(f"[bench] timed {a.steps} steps: {wall / a.steps * 1e3:.3f} ms/step, forward execute "
-          f"{exe_ms * 1e3:.1f} us (K rotation {rot_ms * 1e3:.1f}, attention kernel {att_ms * 1e3:.1f}), "
-          f"decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    # the layout prepasses, timed apart
+    # the execute without an event between its two launches (100 back to
+    # back), reported beside the timed region's
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(100):
+        fwd.execute()
+    e1.record()
+    torch.cuda.synchronize()
+    exe_b2b_ms = e0.elapsed_time(e1) / 100
+    print(f"[bench] timed {a.steps} steps: {wall / a.steps * 1e3:.3f} ms/step, forward execute "
+          f"{exe_ms * 1e3:.1f} us (K rotation {rot_ms * 1e3:.1f}, attention kernel {att_ms * 1e3:.1f}; "
+          f"{exe_b2b_ms * 1e3:.1f} back to back), decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    # the layout prepasses, timed apart
     torch.cuda.synchronize()
     e0.record()
     for _ in range(50):
@@ -631,6 +640,7 @@ def main(argv=None):
             "execute_us": round(exe_ms * 1e3, 2),
             "k_rotation_us": round(rot_ms * 1e3, 2),
             "attention_us": round(att_ms * 1e3, 2),
+            "execute_us_back_to_back": round(exe_b2b_ms * 1e3, 2),
             "plan_us_once_per_layout": round(plan_us, 2),
         },
         "decode": {
