@@ -872,3 +872,43 @@ def test_fwd_graph_replay(S):
         if i == 0:
             ref, _ = oracle_fwd(c)
             assert_parity("bf16", o_graph, ref, f"graph replay S={S}")
+
+
+def test_fwd_repeated_calls_share_poisoned_workspace():
+    """Forward calls of every mask kind, dtype and size class (one-launch
+    short rows, the K pass, a broadcast mask, segments of one row, causal,
+    fp32) through one workspace that starts as all-ones bytes, twice over in
+    opposite orders, each checked against the oracle: nothing a call reads
+    from its workspace (plan, positions, key bits, rotated K) may be left
+    from before it."""
+    import masked_bidirectional_attention_amd as mz
+    cases = [
+        W.random_fwd(70, 2, 16, 2, 300, 300, 128, "bf16", W.MASK_BOOL, mask_shape="full", rope_base=1e6),
+        W.random_fwd(71, 1, 8, 2, 40, 40, 128, "bf16", W.MASK_NONE, rope_base=1e4),
+        W.random_fwd(72, 2, 8, 8, 257, 513, 64, "f16", W.MASK_BOOL, mask_shape="key", rope_base=1e4,
+                     pe_attn_head=1),
+        W.random_fwd(73, 2, 4, 2, 600, 600, 128, "bf16", W.MASK_SEGMENT, rope_base=1e4, n_segments=5),
+        W.random_fwd(74, 1, 4, 1, 200, 200, 128, "bf16", W.MASK_CAUSAL, rope_base=1e4),
+        W.random_fwd(75, 2, 4, 2, 129, 65, 64, "f32", W.MASK_BOOL, mask_shape="blocky", rope_base=1e4),
+        W.random_fwd(76, 3, 8, 1, 64, 64, 128, "f16", W.MASK_SEGMENT, rope_base=1e4, n_segments=2),
+    ]
+    ws = torch.full((64 << 20,), 255, dtype=torch.uint8, device=DEV)
+    for rep, order in enumerate((cases, cases[::-1])):
+        for c in order:
+            kw = dict(scale=c.scale, rope_base=c.rope_base, pe_attn_head=c.pe_attn_head, rope_style=c.rope_style,
+                      pos_q=dev(c.pos_q), pos_k=dev(c.pos_k), return_lse=True, workspace=ws)
+            if c.mask_kind == W.MASK_BOOL:
+                kw["mask"] = dev(c.mask)
+            elif c.mask_kind == W.MASK_SEGMENT:
+                kw["seg_q"], kw["seg_k"] = dev(c.seg_q), dev(c.seg_k)
+            elif c.mask_kind == W.MASK_CAUSAL:
+                kw["causal"] = True
+            call = mz.FwdCall(dev(c.q), dev(c.k), dev(c.v), **kw)
+            assert call.workspace_bytes <= ws.numel()
+            o, lse = call()
+            torch.cuda.synchronize()
+            ref, lse_ref = oracle_fwd(c)
+            assert_parity(c.dtype, o, ref, f"{c.name} pass {rep}")
+            fin = np.isfinite(lse_ref)
+            assert np.array_equal(np.isfinite(to64(lse)), fin)
+            np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=1e-4 if c.dtype == "f32" else 3e-2)
