@@ -118,21 +118,37 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   const int qi_c = qvalid ? qi : p.Sq - 1;
   const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi_c * p.qs[2];
   const bool rot = h < p.n_rot;  // uniform over the work-group
+  // A wave whose 32 queries all lie past Sq (short rows: 112 of the 128
+  // queries of a 16-token tile) issues none of the loads below.  The test
+  // is wave-uniform (a scalar branch, no per-lane masking), and the vector
+  // memory instructions it saves are what a short row's prologue is bound
+  // by: every wave-wide load costs the compute unit's load path the same
+  // whatever its lanes' addresses.
+  const bool wave_live = qt * BM + __builtin_amdgcn_readfirstlane(wave) * 32 < p.Sq;
   // the query's position: its index, or an array element (a uniform
   // branch before the other loads, so that the table rows, which need it,
   // wait for this load alone, and for nothing when there is no array)
   int qpos = qi_c;
-  if (rot && p.pos_q_mode != POS_ARANGE) qpos = p.pos_q[b * p.pos_q_sb + qi_c];
+  if (rot && wave_live && p.pos_q_mode != POS_ARANGE) qpos = p.pos_q[b * p.pos_q_sb + qi_c];
   const float qsc = p.scale_log2;
+  if (wave_live) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = *(const uint4*)(qrow + s * 16 + hh * 8);
+    for (int s = 0; s < NS; ++s) qf[s] = *(const uint4*)(qrow + s * 16 + hh * 8);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = make_uint4(0u, 0u, 0u, 0u);
+  }
   // RMSNorm of q: this lane holds half of the row (elements s*16 + hh*8
   // + e), lane ^ 32 the other half
   const bool qnorm = p.q_norm_w != nullptr;
-  const uint16_t* wsrc = qnorm ? (const uint16_t*)p.q_norm_w : qrow;
   uint4 wq[NS];
+  if (qnorm && wave_live) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) wq[s] = *(const uint4*)(wsrc + s * 16 + hh * 8);
+    for (int s = 0; s < NS; ++s) wq[s] = *(const uint4*)((const uint16_t*)p.q_norm_w + s * 16 + hh * 8);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wq[s] = make_uint4(0u, 0u, 0u, 0u);
+  }
   // cos / sin of this lane's pairs at the query's position, read from the
   // table as 16-byte vectors, all issued before any is used: interleaved,
   // piece s holds pairs s*8 + hh*4 + t (t < 4), slot 4s + t; half split,
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // direct formula instead (same bits), a branch at the use.
   const bool in_tab = qpos >= 0 && qpos < p.rope_tab_len;
   float4 tb[2 * NS];
-  if (rot) {
+  if (rot && wave_live) {
     const float2* trow = p.rope_tab + (size_t)(in_tab ? qpos : 0) * (D / 2);
     if (p.rope_style == 1) {
 #pragma unroll
@@ -588,24 +604,38 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     // Q prologue; the keys' positions are their indices on this path)
 #pragma unroll
     for (int u = 0; u < NPC; ++u) jr[u] = min(t * BN + (tid + u * 256) / Q8, p.Sk - 1);
-    const uint16_t* wbase = norm ? (const uint16_t*)p.k_norm_w : nullptr;
+    // piece block u covers rows [u * 256 / Q8, (u + 1) * 256 / Q8) of the
+    // tile; a block wholly past Sk loads nothing (a work-group-uniform
+    // branch) and writes zeros
+    bool u_live[NPC];
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) u_live[u] = t * BN + u * (256 / Q8) < p.Sk;
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < NPC; ++u) {
       const int d0 = ((tid + u * 256) % Q8) * 8;
       const uint16_t* row = src + (int64_t)jr[u] * p.ks[2] + d0;
-      const uint16_t* wr = norm ? wbase + d0 : row;  // (a valid address either way)
-      a0[u] = *(const u32x4_t*)row;
-      w0[u] = *(const u32x4_t*)wr;
-      a1[u] = a0[u];
-      w1[u] = w0[u];
-      if constexpr (HALF) {
-        a1[u] = *(const u32x4_t*)(row + D / 2);
-        w1[u] = *(const u32x4_t*)(wr + D / 2);
+      const uint16_t* wr = (const uint16_t*)p.k_norm_w + d0;
+      a0[u] = a1[u] = w0[u] = w1[u] = zero4;
+      if (u_live[u]) {
+        a0[u] = *(const u32x4_t*)row;
+        a1[u] = a0[u];
+        if constexpr (HALF) a1[u] = *(const u32x4_t*)(row + D / 2);
+      }
+      if (norm && u_live[u]) {
+        w0[u] = *(const u32x4_t*)wr;
+        w1[u] = w0[u];
+        if constexpr (HALF) w1[u] = *(const u32x4_t*)(wr + D / 2);
       }
     }
     if (rot) {
 #pragma unroll
       for (int u = 0; u < NPC; ++u) {
+        if (!u_live[u]) {
+#pragma unroll
+          for (int k = 0; k < NP / 2; ++k) tv[u * (NP / 2) + k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          continue;
+        }
         const int d0 = ((tid + u * 256) % Q8) * 8;
         const int pt = jr[u] < p.rope_tab_len ? jr[u] : 0;
         const float4* trow = (const float4*)(p.rope_tab + (size_t)pt * (D / 2) + (HALF ? d0 : d0 / 2));
@@ -620,6 +650,11 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       const int piece = tid + u * 256;
       const int r = piece / Q8, d0 = (piece % Q8) * 8;
       const bool valid = t * BN + r < p.Sk;
+      if (!u_live[u]) {
+        *(uint4*)&kst[r * KS + d0] = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (HALF) *(uint4*)&kst[r * KS + d0 + D / 2] = make_uint4(0u, 0u, 0u, 0u);
+        continue;
+      }
       float x[NE];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = Elem<T>::to_f32((uint16_t)(a0[u][e / 2] >> (16 * (e & 1))));
