@@ -80,8 +80,9 @@ COPY_BYTES = 64 * 1024 * 1024
 
 def pmc_workload():
     """A short run for rocprofv3 --pmc: a plain copy of known size (the
-    counter calibration), then the attention kernel and the decode step of
-    the timed workload, three launches each."""
+    counter calibration), then the forward execute of the timed workload,
+    the attention kernel on dense 2048-token rows and the decode step of the
+    timed workload, three launches each."""
     import torch
     import masked_bidirectional_attention_amd as mz
     from masked_bidirectional_attention_amd import workloads as W
@@ -102,13 +103,26 @@ def pmc_workload():
     for _ in range(3):
         fwd.execute()
     torch.cuda.synchronize()
+    # dense rows, every work-group the same length (B 2, 2048 tokens, Hq 16
+    # / Hkv 8, no mask, no RoPE): the per-step figures without load imbalance
+    g = torch.Generator().manual_seed(5)
+    qd, kd, vd = (torch.randn(2, h, 2048, 128, generator=g).to(torch.bfloat16).to(dev) for h in (16, 8, 8))
+    dense = mz.FwdCall(qd, kd, vd)
+    dense.plan()
+    for _ in range(3):
+        dense.attend()
+    torch.cuda.synchronize()
     for kc, vc in copies:
         mz.mzattn_decode(dq, kc, vc, span=8192, mask=dmask, scale=c4.scale)
     torch.cuda.synchronize()
     print("pmc workload done", flush=True)
 
 
-TRAFFIC_KERNELS = (("fwd_mfma_kernel", "fwd_mfma_kernel"), ("k_rotate16_kernel", "k_rotate16_kernel"),
+# (key, kernel-name pattern): the packed workload's attention kernel is the
+# segment-kind instance, the dense rows' the no-mask one
+TRAFFIC_KERNELS = (("fwd_mfma_kernel", "fwd_mfma_kernel<mz::BF16, 128, 2,"),
+                   ("fwd_mfma_kernel_dense", "fwd_mfma_kernel<mz::BF16, 128, 0,"),
+                   ("k_rotate16_kernel", "k_rotate16_kernel"),
                    ("decode_mfma_kernel", "decode_mfma_kernel"), ("decode_merge16_kernel", "decode_merge16_kernel"))
 SIMDS = 1024  # 256 compute units x 4 SIMDs
 XCDS = 8
@@ -372,10 +386,10 @@ def main(argv=None):
     # the same cold cache copies under the mask of fill L, at the full span
     # and at the span rounded up to 256
     by_fill = []
-    for L in (257, 1024, 3100):
+    for L in (257, 1024, 3100, 8192):
         mask_l = torch.zeros_like(dmask)
         mask_l[..., :L] = True
-        for span in (8192, W.ceil256(L)):
+        for span in sorted({8192, W.ceil256(L)}, reverse=True):
             # eager (events around each call, host launch included) and as a
             # replayed graph of 8 calls over 8 cold cache copies (GPU time)
             dl = mz.DecodeCall(dq, kc0, vc0, span=span, mask=mask_l, scale=c4.scale)
@@ -415,6 +429,46 @@ def main(argv=None):
                             "GB/s": round(decode_bytes(L, span) / (us * 1e-6) / 1e9, 1),
                             "GB/s_graph": round(decode_bytes(L, span) / (gus * 1e-6) / 1e9, 1),
                             "algorithmic_mb": round(decode_bytes(L, span) / 1e6, 3)})
+    # ---- what one launch that moves the decode step's bytes costs here: a
+    # plain device copy of half of them (8.4 MB read, 8.4 MB written) from 32
+    # rotating cold sources, eager (events around each launch) and as a
+    # replayed graph of 8 copies; the decode step is two dependent launches
+    half = decode_bytes() // 2 // 2
+    fsrc = [torch.empty(half, dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(32)]
+    fdst = torch.empty(half, dtype=torch.bfloat16, device=dev)
+    for i in range(5):
+        fdst.copy_(fsrc[i])
+    torch.cuda.synchronize()
+    tot = 0.0
+    nfl = 64
+    for i in range(nfl):
+        e0.record()
+        fdst.copy_(fsrc[i % 32])
+        e1.record()
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1)
+    floor_us = tot / nfl * 1e3
+    gs = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for i in range(8):
+            fdst.copy_(fsrc[8 + i])
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(6):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    floor_graph_us = e0.elapsed_time(e1) / (6 * 8) * 1e3
+    del g, fsrc, fdst
+    floor = {"what": "one torch device copy moving the decode step's 16.81 MB (half read, half written), "
+                     "cold sources; the decode step itself is two dependent launches",
+             "us": round(floor_us, 2), "graph_us": round(floor_graph_us, 2),
+             "GB/s": round(decode_bytes() / (floor_us * 1e-6) / 1e9, 1),
+             "GB/s_graph": round(decode_bytes() / (floor_graph_us * 1e-6) / 1e9, 1)}
+
     # ---- causal prefill (reported, not the headline): the same kernel under
     # the causal kind, K rotation + attention per call, layout planned once
     cp = W.vox_prefill_causal()
@@ -658,6 +712,7 @@ def main(argv=None):
                 "algorithmic_mb": round(decode_bytes() / 1e6, 3),
             },
             "by_fill": by_fill,
+            "one_launch_copy_floor": floor,
         },
         "other_forward": other_fwd,
         "causal_prefill": causal,
