@@ -192,15 +192,19 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       const uint32_t w2 = e < 4 ? (e < 2 ? wq[s].x : wq[s].y) : (e < 6 ? wq[s].z : wq[s].w);
       return x * qinv * Elem<T>::to_f32((uint16_t)(w2 >> (16 * (e & 1))));
     };
-    auto cs_at = [&](int m, int pair) -> float2 {
+    // cos / sin of slot m (pair index pair); DIRECT: a lane whose position
+    // lies past the table takes the direct formula (same bits)
+    auto cs_at = [&](auto direct, int m, int pair) -> float2 {
       const float4 v = tb[m >> 1];
       float2 cs = (m & 1) ? make_float2(v.z, v.w) : make_float2(v.x, v.y);
-      if (__builtin_expect(!in_tab, 0)) cs = rope_cs_direct(qpos, pair, D, p.rs);
+      if constexpr (decltype(direct)::value) {
+        if (!in_tab) cs = rope_cs_direct(qpos, pair, D, p.rs);
+      }
       return cs;
     };
-    if (qvalid && rot && p.rope_style == 1) {
-      // half split: element e of chunk s pairs with element e of chunk
-      // s + NS/2 (d and d + D/2), both held by this lane
+    // half split: element e of chunk s pairs with element e of chunk
+    // s + NS/2 (d and d + D/2), both held by this lane
+    auto half_split = [&](auto direct) {
 #pragma unroll
       for (int s = 0; s < NS / 2; ++s) {
         uint32_t lo[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           for (int e = 0; e < 2; ++e) {
             const float a = qn(Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e))), s, 2 * t + e);
             const float c = qn(Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e))), s + NS / 2, 2 * t + e);
-            const float2 cs = cs_at(8 * s + 2 * t + e, s * 16 + hh * 8 + 2 * t + e);
+            const float2 cs = cs_at(direct, 8 * s + 2 * t + e, s * 16 + hh * 8 + 2 * t + e);
             r[0][e] = fmaf(a, cs.x, -c * cs.y);
             r[1][e] = fmaf(c, cs.x, a * cs.y);
           }
@@ -222,8 +226,9 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         qf[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         qf[s + NS / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
-    } else if (qvalid) {
-      // interleaved: the pairs are the two halves of each 32-bit word
+    };
+    // interleaved: the pairs are the two halves of each 32-bit word
+    auto interleaved = [&](auto rotate, auto direct) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
@@ -232,8 +237,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         for (int t = 0; t < 4; ++t) {
           float a = qn(Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), s, 2 * t);
           float c = qn(Elem<T>::to_f32((uint16_t)(wv[t] >> 16)), s, 2 * t + 1);
-          if (rot) {
-            const float2 cs = cs_at(4 * s + t, d0 / 2 + t);
+          if constexpr (decltype(rotate)::value) {
+            const float2 cs = cs_at(direct, 4 * s + t, d0 / 2 + t);
             const float ra = fmaf(a, cs.x, -c * cs.y);
             const float rc = fmaf(c, cs.x, a * cs.y);
             a = ra;
@@ -243,6 +248,24 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         }
         qf[s] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
+    };
+    // Every lane of a live wave runs the same code (a lane past Sq holds a
+    // copy of row Sq - 1 and its result is never stored), so each branch
+    // here is uniform over the wave: no per-lane masking around the
+    // arithmetic.  The direct formula is compiled in only for a wave with a
+    // position past the table.
+    if (!wave_live) return;
+    using yes = std::true_type;
+    using no = std::false_type;
+    const bool direct = !__all(in_tab);
+    if (rot && p.rope_style == 1) {
+      if (direct) half_split(yes{});
+      else half_split(no{});
+    } else if (rot) {
+      if (direct) interleaved(yes{}, yes{});
+      else interleaved(yes{}, no{});
+    } else {
+      interleaved(no{}, no{});
     }
   };
 
