@@ -131,7 +131,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   int qpos = qi_c;
   if (rot && wave_live && p.pos_q_mode != POS_ARANGE) qpos = p.pos_q[b * p.pos_q_sb + qi_c];
   const float qsc = p.scale_log2;
-  if (wave_live) {
+  // (the one-tile kernels load the q row on every wave: a skipped load's
+  // registers merge with the loaded ones, and that merge waits for the
+  // loads before the cos / sin and K loads can issue, a round trip these
+  // one-step launches cannot hide; measured 0.4 us per 16-token launch.
+  // The multi-tile kernels keep the skip: there it measured ~1 % faster.)
+  if (KR != 0 || wave_live) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const uint4*)(qrow + s * 16 + hh * 8);
   } else {
