@@ -54,6 +54,25 @@ template <int D> struct Lay {
 // most this many tiles; longer rows read them from global memory.
 constexpr int CLS_LDS = 4096;
 
+// Causal kind: which query tile the slot-th work item of a (batch,
+// kv-head) unit takes.  Query tile t has ~2t + 2 key tiles, so a plain
+// order hands each XCD (a contiguous range of slots) only long or only
+// short tiles.  When each XCD holds C (even) whole slots of one unit, the
+// XCD's C slots take C/2 tiles from the long end, longest first, then C/2
+// from the short end, shortest first: every XCD gets the same work, and the
+// two work-groups the dispatcher places on one CU (its i-th and (C/2 + i)-
+// th slots' heads) pair a long tile with a short one.  Otherwise the tiles
+// go longest first.
+__device__ inline int causal_query_tile(int slot, int n_qt, int nwork, int G) {
+  const int per_xcd = (nwork & 7) == 0 ? nwork >> 3 : 0;
+  const int C = per_xcd % G == 0 ? per_xcd / G : 0;
+  if (C >= 2 && (C & 1) == 0 && n_qt % C == 0) {
+    const int c = slot / C, r = slot % C, h = C / 2;
+    return r < h ? n_qt - 1 - (c * h + r) : c * h + (r - h);
+  }
+  return n_qt - 1 - slot;
+}
+
 // NSTR key streams per work-group.  With NSTR 2 the work-group has 8 waves:
 // waves w and w + 4 own the same 32 queries and take alternate live key
 // tiles (each stream with its own copies and LDS stages), and the two
@@ -91,8 +110,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   const int nwork = p.B * p.Hq * p.n_qt;
   const int w = xcd_remap(blockIdx.x, nwork);
   const int g = w % p.G;
-  // causal: the last query tiles have the most keys, so they start first
-  const int qt = MK == 3 ? p.n_qt - 1 - (w / p.G) % p.n_qt : (w / p.G) % p.n_qt;
+  const int qt = MK == 3 ? causal_query_tile((w / p.G) % p.n_qt, p.n_qt, nwork, p.G) : (w / p.G) % p.n_qt;
   const int kvb = w / (p.G * p.n_qt);
   const int b = kvb % p.B, hk = kvb / p.B;
   const int h = hk * p.G + g;
