@@ -912,3 +912,30 @@ def test_fwd_repeated_calls_share_poisoned_workspace():
             fin = np.isfinite(lse_ref)
             assert np.array_equal(np.isfinite(to64(lse)), fin)
             np.testing.assert_allclose(to64(lse)[fin], lse_ref[fin], atol=1e-4 if c.dtype == "f32" else 3e-2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 100, 140, 128), (2, 16, 2, 16, 16, 128), (1, 8, 1, 40, 64, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_query_positions_past_the_table(dtype, style, shape):
+    """Explicit query positions, some inside the cos/sin table (which covers
+    max(Sq, Sk) positions) and some far past it, in both pairings: a wave
+    whose positions all lie in the table reads it, any other wave takes the
+    direct formula for its lanes past it.  Rows of one key tile (the last
+    two shapes) take the one-launch path (key positions default)."""
+    import masked_bidirectional_attention_amd as mz
+    B, Hq, Hkv, Sq, Sk, D = shape
+    seed = zlib.crc32(repr((dtype, style, shape)).encode()) % 10000
+    case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_NONE, rope_base=1e4)
+    rng = np.random.default_rng(seed)
+    pos_q = rng.integers(0, max(Sq, Sk), size=(B, Sq)).astype(np.int32)
+    far = rng.random((B, Sq)) < 0.3
+    pos_q[far] = rng.integers(5000, 60000, size=int(far.sum()))
+    pos_q[0, :min(Sq, 32)] = np.arange(min(Sq, 32))   # one wave wholly inside the table
+    pq = torch.from_numpy(pos_q)
+    o = mz.mzattn_fwd(dev(case.q), dev(case.k), dev(case.v), rope_base=1e4, rope_style=style, pos_q=dev(pq))
+    torch.cuda.synchronize()
+    ref, _ = mzref.mzref_fwd(dtype, W.to_bits(case.q), W.to_bits(case.k), W.to_bits(case.v), rope_base=1e4,
+                             rope_style=style, pos_q=pos_q, pos_k=np.arange(Sk, dtype=np.int32)[None].repeat(B, 0))
+    assert_parity(dtype, o, ref, f"positions past the table {style} {shape}")
