@@ -126,12 +126,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // the norm weights, the cos / sin table entries) are issued here; the
   // arithmetic (finish_q) runs once the first K / V tile copies are
   // issued, so the two latencies overlap.
-  // Every load here is unconditional and outside any per-lane branch
-  // (a lane past Sq reads row Sq - 1, absent norm weights read the q row
-  // itself; neither result is used): a load inside a per-lane branch ends
-  // in a wait for everything issued before it, which would make the
-  // prologue a chain of round trips.  A position array is read first, so
-  // the table rows that depend on it wait for it alone.
+  // No load here sits inside a per-lane branch (a lane past Sq reads row
+  // Sq - 1, and its result is never stored): such a load ends in a wait for
+  // everything issued before it, which would make the prologue a chain of
+  // round trips.  Loads nobody needs (absent norm weights, waves with no
+  // query) are skipped by wave-uniform branches only.  A position array is
+  // read first, so the table rows that depend on it wait for it alone.
   uint4 qf[NS];
   const int qi_c = qvalid ? qi : p.Sq - 1;
   const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi_c * p.qs[2];
