@@ -23,7 +23,8 @@ around the whole execute in the odd timed steps; ``roofline`` that of the
 attention kernel alone, timed with an event between the two launches in
 the even steps; ``decode`` the static-cache step's HBM GB/s, each against
 MI355X's published peaks, and ``cpu_baseline`` the fp64 oracle timed on
-the host for full packed-workload calls.
+the host for full packed-workload calls (with the F5-style layer, the
+padded pair and the decode step beside it).
 """
 from __future__ import annotations
 
@@ -50,6 +51,11 @@ def live_pairs_packed():
 def fwd_flops():
     """4 * D per live (query, key) pair: 2 for Q.K^T and 2 for P.V."""
     return 4 * 128 * live_pairs_packed()
+
+
+# live flops of the F5-style layer: B 2 x H 16 x 1500 queries, row 0 sees
+# 1500 keys and row 1 1200, 4 * D (64) per live pair
+F5_GFLOP = 4 * 64 * 16 * 1500 * (1500 + 1200) / 1e9
 
 
 def decode_bytes(L=8192, span=8192):
@@ -231,7 +237,9 @@ def cpu_baseline():
     """The fp64 numpy oracle (never tuned for speed) on the host, on a
     bounded sample of the packed-guidance workload: the full forward with
     every BLAS thread (nproc) and a 2-head slice single-threaded, each the
-    median of 3 timed runs, scaled to live TFLOP/s."""
+    median of 3 timed runs, scaled to live TFLOP/s; and the other
+    configurations (F5-style layer, padded pair, decode step at L 8192)
+    whole with every thread, median of 3, in s per call."""
     import statistics
     import threadpoolctl
     from masked_bidirectional_attention_amd import workloads as W
@@ -257,6 +265,31 @@ def cpu_baseline():
         single = statistics.median(run(sub) for _ in range(3))
     f_full = fwd_flops()
     f_sub = f_full * len(sub) / 16
+    # the other configurations, whole, with every BLAS thread, median of 3
+    others = {}
+    with threadpoolctl.threadpool_limits(limits=nproc, user_api="blas"):
+        c1 = W.f5_dit_layer()
+        c2 = W.qwen_cfg_padded()
+        for name, cf, gflop in (("f5_dit_layer", c1, F5_GFLOP), ("qwen_padded", c2, fwd_flops() / 1e9)):
+            args = (cf.dtype, W.to_bits(cf.q), W.to_bits(cf.k), W.to_bits(cf.v))
+            kw = dict(scale=cf.scale, rope_base=cf.rope_base, pe_attn_head=cf.pe_attn_head, mask_kind=cf.mask_kind,
+                      mask=cf.mask.numpy())
+
+            def run_cfg():
+                t0 = time.perf_counter()
+                mzref.mzref_fwd(*args, **kw)
+                return time.perf_counter() - t0
+            sec = statistics.median(run_cfg() for _ in range(3))
+            others[name] = {"s_per_call": round(sec, 3), "TFLOP/s": round(gflop / sec / 1e3, 4)}
+        c4 = W.vox_decode(8192)
+        dargs = (c4.dtype, W.to_bits(c4.q), W.to_bits(c4.k_cache), W.to_bits(c4.v_cache))
+
+        def run_dec():
+            t0 = time.perf_counter()
+            mzref.mzref_decode(*dargs, span=8192, mask=c4.mask.numpy(), scale=c4.scale)
+            return time.perf_counter() - t0
+        sec = statistics.median(run_dec() for _ in range(3))
+        others["vox_decode_L8192"] = {"s_per_call": round(sec, 4), "GB/s": round(decode_bytes() / sec / 1e9, 2)}
     return {
         "value": f_full / multi / 1e12,
         "unit": "TFLOP/s",
@@ -267,6 +300,7 @@ def cpu_baseline():
         "single_thread": {"value": f_sub / single / 1e12, "unit": "TFLOP/s", "cores": 1,
                           "sample": f"heads {sub} of the same forward ({f_sub / 1e9:.2f} live GFLOP), one BLAS "
                                     f"thread: median of 3 runs {single:.2f} s"},
+        "other_configs": others,
         "nproc": nproc,
         "cpu_model": _cpu_model(),
     }
@@ -538,7 +572,7 @@ def main(argv=None):
                 "attention_frac": round(gflop / att * 1e3 / peak, 4)}
 
     f5 = W.f5_dit_layer()
-    f5_gflop = 4 * 64 * 16 * 1500 * (1500 + 1200) / 1e9
+    f5_gflop = F5_GFLOP
     other_fwd = {
         "f5_dit_layer": {"workload": "F5-style DiT layer: B 2 (CFG), H 16, S 1500, D 64, fp16, RoPE base 1e4 on "
                                      "head 0 only, row 1 keys 1200-1499 masked ([2,1,1,1500] bool)",
