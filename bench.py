@@ -770,7 +770,7 @@ def main(argv=None):
         "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
                                       "length on the device, RoPE base 1e4 on q and the new key",
                           "by_fill": append},
-        "device": props.name,
+        "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)",
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host ...", file=sys.stderr, flush=True)
