@@ -377,7 +377,9 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     const int ch = q % nch;
     return (uint32_t)((row * stride + (ch < CH ? ch : 0) * 8) * 2);
   };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // (the "& 3" tells the compiler wave_u < 4, so a slot test that holds for
+  // every wave folds away instead of costing a branch per copy)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave) & 3;
 #pragma unroll
   for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride);
 #pragma unroll
@@ -405,18 +407,20 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       if (u * 4 + wave_u < VINS) lds_dma16_b(d, voff[u], vdst + (u * 4 + wave_u) * 1024);
   };
   // the copies of one step spread over its MFMA slots: slot u < KPW is K
-  // copy instruction u of this wave, slot KPW + u V copy u
+  // copy instruction u of this wave, slot KPW + u V copy u.  Every step
+  // issues all of them (no per-copy branch: those cost more than the copy
+  // they would skip), so only a slot past the tile's instruction count for
+  // this wave is tested.
   struct DmaPlan {
     u32x4_t dk, dv;
     uint32_t kdst, vdst;
-    bool k_on, v_on;
   };
   auto dma_slot = [&](const DmaPlan& pl, int slot) {
     if (slot < KPW) {
-      if (pl.k_on && slot * 4 + wave_u < KINS) lds_dma16_b(pl.dk, koff[slot], pl.kdst + (slot * 4 + wave_u) * 1024);
+      if (slot * 4 + wave_u < KINS) lds_dma16_b(pl.dk, koff[slot], pl.kdst + (slot * 4 + wave_u) * 1024);
     } else {
       const int u = slot - KPW;
-      if (pl.v_on && u * 4 + wave_u < VINS) lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
+      if (u * 4 + wave_u < VINS) lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
     }
   };
 
@@ -804,13 +808,13 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     __syncthreads();
   };
   int j = 0;
-  // copies of one step: K of t(j+2) and V of t(j+1)
+  // copies of one step: K of t(j+2) and V of t(j+1).  On the last steady
+  // step there is no t(j+2); K of t(j+1) is copied again instead, into the
+  // stage that held K of t(j), which no later step reads.
   auto plan_step = [&](int kn2) {
     DmaPlan pl;
-    pl.k_on = kn2 < kt_end;
-    pl.dk = tile_desc(kbase, kstride, pl.k_on ? kn2 : kn);
+    pl.dk = tile_desc(kbase, kstride, kn2 < kt_end ? kn2 : kn);
     pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
-    pl.v_on = true;
     pl.dv = tile_desc(vbase, vstride, kn);
     pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
     return pl;
