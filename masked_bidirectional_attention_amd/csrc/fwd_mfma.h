@@ -41,13 +41,27 @@ __device__ inline int query_position(const FwdParams& p, int b, int i) {
 // ---------------------------------------------------------------------------
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 
-// LDS row layout of the K and V tiles: K rows D + 8 elements apart, V rows
-// D + 32 apart.  With 64 four-byte banks, the 16 K rows one operand fetch
-// touches (same 16-byte chunk) then start 4 banks apart, and the 4 V rows a
-// transposing read touches (64 bytes each per pair of lane groups) 16 banks
-// apart, so neither access has bank conflicts.
+// LDS layout of the 64-row K and V tiles (64 four-byte banks, 256 bytes a
+// cycle).  Each copy instruction (1 KB) reads whole rows from global
+// memory, so it touches as few cache lines as the rows allow.
+//  K: rows KS = D + 8 elements apart (one 16-byte pad chunk, filled with a
+//     copy of chunk 0).  An operand fetch reads one chunk of 16
+//     consecutive rows per 16 lanes, and those start 4 banks apart.
+//  V: no padding.  Groups of 4 rows (one copy instruction at D 128, half of
+//     one at D 64); inside a group, quads of 4 chunks, then the row, then
+//     the chunk.  A transposing read takes 4 rows x 4 chunks per 32 lanes
+//     (two lanes per chunk): 256 contiguous bytes.  v_at is the element
+//     offset of chunk c (elements 8c .. 8c + 7) of row r; copy slot s (the
+//     s-th 16 bytes of the tile) holds chunk v_chunk(s) of row v_row(s).
 template <int D> struct Lay {
-  static constexpr int KS = D + 8, VS = D + 32;
+  static constexpr int CH = D / 8;  // chunks per row
+  static constexpr int KS = D + 8;
+  static_assert(CH % 4 == 0, "whole chunk quads per row");
+  __device__ static constexpr int v_at(int r, int c) {
+    return (r >> 2) * (4 * D) + (c >> 2) * 128 + (r & 3) * 32 + (c & 3) * 8;
+  }
+  __device__ static constexpr int v_row(int s) { return (s / (4 * CH)) * 4 + ((s >> 2) & 3); }
+  __device__ static constexpr int v_chunk(int s) { return ((s % (4 * CH)) >> 4) * 4 + (s & 3); }
 };
 
 // Tile class bytes kept in LDS (boolean-mask mode) when the key axis has at
@@ -92,14 +106,15 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   constexpr int NS = D / 16;  // k-steps of K Q^T
   constexpr int ND = D / 32;  // 32-row d blocks of O^T
   constexpr int CH = D / 8;   // 16-byte chunks of data per row
-  constexpr int KS = Lay<D>::KS, VS = Lay<D>::VS;
-  constexpr int KCH = KS / 8, VCH = VS / 8;  // 16-byte slots per padded row
-  // one direct-to-LDS wave instruction fills 64 consecutive slots (1 KB);
-  // a padded tile of 64 rows takes KCH (VCH) of them
-  constexpr int KINS = KCH, VINS = VCH;
-  constexpr int KPW = (KINS + 3) / 4, VPW = (VINS + 3) / 4;  // per wave, at most
+  using L = Lay<D>;
+  constexpr int KS = L::KS, KCH = KS / 8;  // K: 16-byte slots per padded row
+  // one direct-to-LDS wave instruction fills 64 consecutive copy slots
+  // (1 KB); a K tile takes KCH of them, a V tile CH
+  constexpr int KINS = KCH, VINS = CH;
+  constexpr int KPW = (KINS + 3) / 4, VPW = VINS / 4;  // per wave, at most
+  static_assert(VINS % 4 == 0, "every wave issues the same V copies");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NSTR][2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTR][2][BN * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NSTR][2][BN * D];
   __shared__ uint8_t cls_lds[MK == 1 ? CLS_LDS : 1];
   __shared__ int n_live_lds;
 
@@ -364,26 +379,28 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     if (lane == 0 && c != 0) atomicAdd(&n_live_lds, c);
   }
 
-  // ---- direct-to-LDS tile loads.  Slot q of a padded tile is row q / KCH,
-  // chunk q % KCH; pad slots (chunk >= CH) load chunk 0 of their row again.
-  // The per-lane byte offsets from the tile's first row are fixed (row
-  // strides are below 2^24 elements, so a 64-row tile spans less than 2^31
-  // bytes); only the last tile, whose rows past Sk load row Sk - 1 instead
-  // (their keys are masked), needs them recomputed.
+  // ---- direct-to-LDS tile loads.  Lane i of copy instruction u fills slot
+  // u * 64 + i of the tile: K slot q is row q / KCH, chunk q % KCH (the pad
+  // slot, chunk CH, loads chunk 0 again); V slots as Lay places them.  The
+  // per-lane byte offsets from the tile's first row are the same for every
+  // tile (row strides are below 2^24 elements, so a 64-row tile spans less
+  // than 2^31 bytes); rows past Sk read as zeros through the tile's
+  // descriptor.
   uint32_t koff[KPW], voff[VPW];
-  auto slot_off = [&](int ins, int nch, int64_t stride) -> uint32_t {
-    const int q = ins * 64 + lane;
-    const int row = q / nch;
-    const int ch = q % nch;
-    return (uint32_t)((row * stride + (ch < CH ? ch : 0) * 8) * 2);
-  };
   // (the "& 3" tells the compiler wave_u < 4, so a slot test that holds for
   // every wave folds away instead of costing a branch per copy)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave) & 3;
 #pragma unroll
-  for (int u = 0; u < KPW; ++u) koff[u] = slot_off(u * 4 + wave_u, KCH, kstride);
+  for (int u = 0; u < KPW; ++u) {
+    const int q = (u * 4 + wave_u) * 64 + lane;
+    const int ch = q % KCH;
+    koff[u] = (uint32_t)(((q / KCH) * kstride + (ch < CH ? ch : 0) * 8) * 2);
+  }
 #pragma unroll
-  for (int u = 0; u < VPW; ++u) voff[u] = slot_off(u * 4 + wave_u, VCH, vstride);
+  for (int u = 0; u < VPW; ++u) {
+    const int q = (u * 4 + wave_u) * 64 + lane;
+    voff[u] = (uint32_t)((L::v_row(q) * vstride + L::v_chunk(q) * 8) * 2);
+  }
   const uint32_t ks_lds = lds_addr(&Ks[str][0][0]), vs_lds = lds_addr(&Vs[str][0][0]);
   // descriptor of one K or V tile: its rows below Sk only, so rows past Sk
   // read as zeros (their keys are masked)
@@ -401,16 +418,15 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   };
   auto load_v = [&](int kt, int stage) {
     const u32x4_t d = tile_desc(vbase, vstride, kt);
-    const uint32_t vdst = vs_lds + stage * (BN * VS * 2);
+    const uint32_t vdst = vs_lds + stage * (BN * D * 2);
 #pragma unroll
-    for (int u = 0; u < VPW; ++u)
-      if (u * 4 + wave_u < VINS) lds_dma16_b(d, voff[u], vdst + (u * 4 + wave_u) * 1024);
+    for (int u = 0; u < VPW; ++u) lds_dma16_b(d, voff[u], vdst + (u * 4 + wave_u) * 1024);
   };
   // the copies of one step spread over its MFMA slots: slot u < KPW is K
   // copy instruction u of this wave, slot KPW + u V copy u.  Every step
-  // issues all of them (no per-copy branch: those cost more than the copy
-  // they would skip), so only a slot past the tile's instruction count for
-  // this wave is tested.
+  // issues all of them, with no branch (a branch per copy costs more than
+  // the copy it would skip) but the one for the K instruction that only
+  // some waves have.
   struct DmaPlan {
     u32x4_t dk, dv;
     uint32_t kdst, vdst;
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       if (slot * 4 + wave_u < KINS) lds_dma16_b(pl.dk, koff[slot], pl.kdst + (slot * 4 + wave_u) * 1024);
     } else {
       const int u = slot - KPW;
-      if (u * 4 + wave_u < VINS) lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
+      lds_dma16_b(pl.dv, voff[u], pl.vdst + (u * 4 + wave_u) * 1024);
     }
   };
 
@@ -432,6 +448,13 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
   const int grp = lane >> 4, gi = lane & 15, rr = gi >> 2, cc = gi & 3;
+  // element offsets of the operand reads inside a tile (layout: Lay).  K
+  // fragment (kb, s): chunk 2s + hh of row kb*32 + l32.  Transposing V read
+  // (kb, jj, db): 4 elements at d column db*32 + (grp&1)*16 + 4cc of row
+  // kb*32 + jj*16 + 4hh + rr, and of the row 8 further (+ 8 D).
+  auto k_off = [&](int kb, int s) { return (kb * 32 + l32) * KS + (2 * s + hh) * 8; };
+  const int v_lane = L::v_at(4 * hh + rr, (grp & 1) * 2 + (cc >> 1)) + (cc & 1) * 4;
+  auto v_off = [&](int kb, int jj, int db) { return v_lane + kb * 32 * D + jj * 16 * D + db * 128; };
 
   const f32x16_t zero16 = {};
   // scores of two consecutive tiles; the steady-state loop is unrolled by
@@ -452,7 +475,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 a = *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * s + hh) * 8];
+        const uint4 a = *(const uint4*)&kt_lds[k_off(kb, s)];
         sacc[kb] = mfma32<T>(a, qf[s], s == 0 ? (CINIT ? cinit : zero16) : sacc[kb]);
       }
     }
@@ -518,10 +541,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
-          const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
-          const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
-          const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
+          const uint2 a0 = lds_read_tr<T>(&vt_lds[v_off(kb, jj, db)]);
+          const uint2 a1 = lds_read_tr<T>(&vt_lds[v_off(kb, jj, db) + 8 * D]);
           oacc[db] = mfma32<T>(make_uint4(a0.x, a0.y, a1.x, a1.y), pk[kb][jj], oacc[db]);
         }
       }
@@ -577,14 +598,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     uint32_t wv[2][2][4];
     auto kfrag = [&](auto gc) -> uint4 {
       constexpr int g = decltype(gc)::value, ss = g >> 1, kb = g & 1;
-      return *(const uint4*)&kt_lds[(kb * 32 + l32) * KS + (2 * ss + hh) * 8];
+      return *(const uint4*)&kt_lds[k_off(kb, ss)];
     };
     auto vfrag = [&](auto gc) -> uint4 {
       constexpr int g = decltype(gc)::value, kb = g / (2 * ND), jj = (g / ND) & 1, db = g % ND;
-      const int col = db * 32 + (grp & 1) * 16 + 4 * cc;
-      const int r0 = kb * 32 + jj * 16 + 4 * hh + rr;
-      const uint2 a0 = lds_read_tr<T>(&vt_lds[r0 * VS + col]);
-      const uint2 a1 = lds_read_tr<T>(&vt_lds[(r0 + 8) * VS + col]);
+      const uint2 a0 = lds_read_tr<T>(&vt_lds[v_off(kb, jj, db)]);
+      const uint2 a1 = lds_read_tr<T>(&vt_lds[v_off(kb, jj, db) + 8 * D]);
       return make_uint4(a0.x, a0.y, a1.x, a1.y);
     };
     uint4 frk[PF], frv[PF];
@@ -816,7 +835,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     pl.dk = tile_desc(kbase, kstride, kn2 < kt_end ? kn2 : kn);
     pl.kdst = ks_lds + (j & 1) * (BN * KS * 2);
     pl.dv = tile_desc(vbase, vstride, kn);
-    pl.vdst = vs_lds + ((j + 1) & 1) * (BN * VS * 2);
+    pl.vdst = vs_lds + ((j + 1) & 1) * (BN * D * 2);
     return pl;
   };
   // one steady-state step: tile t(j) scores in sc, t(j+1) scores into sn
@@ -860,9 +879,10 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     // one), so stream 1 passes one fewer when the count is odd
     if constexpr (MK == 1) n_live = n_live_lds;  // counted before the prologue barrier
     if (str == 1 && (n_live & 1)) __syncthreads();
-    // every copy and every LDS operand read of both streams is complete:
-    // stream 1 parks (m, l, O^T) in the K stages, lane-major so that each
-    // access is a conflict-free 16-byte one, and stream 0 folds it in
+    // no K stage is read any more (a last P.V, from V stages, may still be
+    // running): stream 1 parks (m, l, O^T) in the K stages, lane-major so
+    // that each access is a conflict-free 16-byte one, and stream 0 folds
+    // it in
     static_assert(sizeof(float) * (4 * ND * 16 * 64 + 2 * 4 * 64) <= sizeof(Ks), "partials fit the K stages");
     float* part = reinterpret_cast<float*>(&Ks[0][0][0]);
     float2* part_ml = reinterpret_cast<float2*>(part + 4 * ND * 16 * 64);
