@@ -567,16 +567,24 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   };
 
   // One exponential piece: 2 of the 32 scores of a lane (tile t(j)), packed
-  // into P block (kb, jj) and added to the row sum.
+  // into P block (kb, jj) and added to the row sum.  The exponentials of a
+  // piece are issued in one K Q^T MFMA slot and packed in the next
+  // (pack_piece), so the wave, which issues in order, does not wait for
+  // their results before its next MFMA (dense rows ~2 % faster).
   constexpr int NQK = 2 * NS, NPV = 4 * ND;
   static_assert(16 % NQK == 0, "exponential pieces spread evenly over the K Q^T MFMAs");
   static_assert(NSLOT <= NPV, "every copy has a P.V slot");
-  auto exp_piece = [&](auto hc, float& lsa, float& lsb, uint32_t (&wv)[2][2][4], f32x16_t (&scur)[2]) {
+  auto exp_pair = [&](auto hc, f32x16_t (&scur)[2]) -> float2 {
     constexpr int h = decltype(hc)::value;
     constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
     const float p0 = fast_exp2(scur[kb][jj * 8 + 2 * e] - (CINIT ? 0.f : mu));
     const float p1 = fast_exp2(scur[kb][jj * 8 + 2 * e + 1] - (CINIT ? 0.f : mu));
-    wv[kb][jj][e] = Elem<T>::pack2(p0, p1);
+    return make_float2(p0, p1);
+  };
+  auto pack_piece = [&](auto hc, float2 pp, float& lsa, float& lsb, uint32_t (&wv)[2][2][4]) {
+    constexpr int h = decltype(hc)::value;
+    constexpr int kb = h >> 3, jj = (h >> 2) & 1, e = h & 3;
+    wv[kb][jj][e] = Elem<T>::pack2(pp.x, pp.y);
     __asm__ volatile("" ::"v"(wv[kb][jj][e]));
     if constexpr (e & 1) lsb = Elem<T>::add_pair(wv[kb][jj][e], lsb);
     else lsa = Elem<T>::add_pair(wv[kb][jj][e], lsa);
@@ -607,6 +615,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       return make_uint4(a0.x, a0.y, a1.x, a1.y);
     };
     uint4 frk[PF], frv[PF];
+    constexpr int PPS = 16 / NQK;  // exponential pieces per K Q^T MFMA slot
+    float2 held[PPS];
     static_for<PF>([&](auto gc) { frk[decltype(gc)::value] = kfrag(gc); });
     static_for<NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value, ss = i >> 1, kb = i & 1;
@@ -614,9 +624,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       if constexpr (i + PF < NQK) frk[i % PF] = kfrag(std::integral_constant<int, i + PF>{});
       else frv[i + PF - NQK] = vfrag(std::integral_constant<int, i + PF - NQK>{});
       snext[kb] = mfma32<T>(f, qf[ss], ss == 0 ? (CINIT ? cinit : zero16) : snext[kb]);
-      static_for<16 / NQK>([&](auto pc) { exp_piece(std::integral_constant<int, i * (16 / NQK) + decltype(pc)::value>{}, lsa, lsb, wv, scur); });
+      if constexpr (i > 0)
+        static_for<PPS>([&](auto pc) { pack_piece(std::integral_constant<int, (i - 1) * PPS + decltype(pc)::value>{}, held[decltype(pc)::value], lsa, lsb, wv); });
+      static_for<PPS>([&](auto pc) { held[decltype(pc)::value] = exp_pair(std::integral_constant<int, i * PPS + decltype(pc)::value>{}, scur); });
       __builtin_amdgcn_sched_barrier(0);
     });
+    static_for<PPS>([&](auto pc) { pack_piece(std::integral_constant<int, (NQK - 1) * PPS + decltype(pc)::value>{}, held[decltype(pc)::value], lsa, lsb, wv); });
     static_for<NPV>([&](auto ic) {
       constexpr int i = decltype(ic)::value, kb = i / (2 * ND), jj = (i / ND) & 1, db = i % ND;
       const uint4 f = frv[i % PF];
