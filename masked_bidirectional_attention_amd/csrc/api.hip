@@ -33,7 +33,6 @@ int ok() {
 
 constexpr int64_t kMaxSeq = int64_t(1) << 20;
 constexpr int kMaxBatch = 65535;
-constexpr int kRopeTableMax = 16384;  // positions held in the cos/sin table
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -68,7 +67,8 @@ struct FwdPlan {
   int n_rot = 0, n_rot_kv = 0, n_rotk = 0, tab_len = 0;
   int Bm = 1, Hm = 1;
   size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_kpos = 0, off_cls = 0;
-  size_t off_bits = 0;
+  size_t off_bits = 0, off_qrows = 0, off_krows = 0;
+  int q_rows_b = 0, k_rows_b = 0;  // batch rows of the cos / sin row arrays (0: none)
   int mask_rows = 0;
   bool need_qpos = false;
   size_t bytes = 0;
@@ -157,11 +157,24 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
   };
   const int D = a->head_dim;
   if (n_rot > 0) {
-    int len = a->seq_q > a->seq_k ? a->seq_q : a->seq_k;
-    if (len > kRopeTableMax) len = kRopeTableMax;
-    if (len < 1) len = 1;
+    // Index positions read the table (positions 0 .. seq - 1 of that side);
+    // explicit or segment-derived positions get per-row arrays, so that no
+    // kernel after the plan needs a position or the direct formula.
+    const bool q_rows = a->pos_q != nullptr || a->mask_kind == MZ_MASK_SEGMENT;
+    const bool k_rows = a->pos_k != nullptr || a->mask_kind == MZ_MASK_SEGMENT;
+    int len = 0;
+    if (!q_rows && a->seq_q > len) len = a->seq_q;
+    if (!k_rows && a->seq_k > len) len = a->seq_k;
     pl->tab_len = len;
-    pl->off_tab = carve((size_t)len * (D / 2) * sizeof(float) * 2);
+    if (len > 0) pl->off_tab = carve((size_t)len * (D / 2) * sizeof(float) * 2);
+    if (q_rows) {
+      pl->q_rows_b = (a->pos_q != nullptr && a->pos_q_stride_b == 0) ? 1 : a->batch;
+      pl->off_qrows = carve((size_t)pl->q_rows_b * a->seq_q * (D / 2) * sizeof(float) * 2);
+    }
+    if (k_rows) {
+      pl->k_rows_b = (a->pos_k != nullptr && a->pos_k_stride_b == 0) ? 1 : a->batch;
+      pl->off_krows = carve((size_t)pl->k_rows_b * a->seq_k * (D / 2) * sizeof(float) * 2);
+    }
   }
   if (pl->n_rot_kv > 0) pl->off_krot = carve((size_t)a->batch * pl->n_rot_kv * a->seq_k * D * elem_size(a->dtype));
   if (a->mask_kind == MZ_MASK_SEGMENT) {
@@ -336,8 +349,24 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   p.rope_style = a->rope_style;
   if (pl.n_rot > 0) {
     p.rs = rope_spec(a->rope_base, a->rope_precision, a->rope_mscale, a->rope_factors);
-    p.rope_tab = reinterpret_cast<float2*>(ws + pl.off_tab);
+    p.rope_tab = pl.tab_len > 0 ? reinterpret_cast<float2*>(ws + pl.off_tab) : nullptr;
     p.rope_tab_len = pl.tab_len;
+    if (pl.q_rows_b > 0) {
+      p.q_rows = reinterpret_cast<float2*>(ws + pl.off_qrows);
+      p.q_rows_b = pl.q_rows_b;
+      p.q_cs = p.q_rows;
+      p.q_cs_sb = pl.q_rows_b == 1 ? 0 : a->seq_q;
+    } else {
+      p.q_cs = p.rope_tab;
+    }
+    if (pl.k_rows_b > 0) {
+      p.k_rows = reinterpret_cast<float2*>(ws + pl.off_krows);
+      p.k_rows_b = pl.k_rows_b;
+      p.k_cs = p.k_rows;
+      p.k_cs_sb = pl.k_rows_b == 1 ? 0 : a->seq_k;
+    } else {
+      p.k_cs = p.rope_tab;
+    }
     if (a->pos_q) { p.pos_q_mode = mz::POS_ARRAY; p.pos_q = a->pos_q; p.pos_q_sb = a->pos_q_stride_b; }
     else if (a->mask_kind == MZ_MASK_SEGMENT) {
       p.pos_q_mode = mz::POS_SEGMENT; p.pos_q = reinterpret_cast<int32_t*>(ws + pl.off_qpos); p.pos_q_sb = a->seq_q;

@@ -16,17 +16,45 @@
 namespace mz {
 
 // ---------------------------------------------------------------------------
-// Prepass 1: cos/sin table of the rotary angles, positions [0, len).
+// Prepass 1: cos/sin of the rotary angles, one launch for three ranges of
+// rows (all by the same formula, so a position gives the same bits
+// wherever it is held):
+//   the table, row j = position j, j < tab_len (index positions read it);
+//   the query rows, row b * Sq + i = position pos_q[b * pos_q_sb + i], for
+//   q_rows_b batch rows, when the positions are given or derived from
+//   segments;
+//   the key rows likewise.
+// The kernels after the plan read these rows and need neither the
+// positions nor the direct formula.  In segment mode it runs after the
+// segment prepass, which derives the positions.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int len, int D, const RopeSpec rs) {
+__global__ __launch_bounds__(256) void rope_prep_kernel(const FwdParams p) {
   __shared__ double theta[64];
-  const int half = D / 2;
-  if (threadIdx.x < half) theta[threadIdx.x] = rope_theta(threadIdx.x, D, rs);
+  const int half = p.D / 2;
+  if (threadIdx.x < half) theta[threadIdx.x] = rope_theta(threadIdx.x, p.D, p.rs);
   __syncthreads();
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)len * half) return;
-  const int pos = (int)(idx / half), i = (int)(idx % half);
-  tab[idx] = rope_cs_theta(pos, theta[i], rs);
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_tab = (int64_t)p.rope_tab_len * half;
+  const int64_t n_q = p.q_rows != nullptr ? (int64_t)p.q_rows_b * p.Sq * half : 0;
+  const int64_t n_k = p.k_rows != nullptr ? (int64_t)p.k_rows_b * p.Sk * half : 0;
+  const int i = (int)(idx % half);
+  if (idx < n_tab) {
+    p.rope_tab[idx] = rope_cs_theta((int)(idx / half), theta[i], p.rs);
+    return;
+  }
+  idx -= n_tab;
+  if (idx < n_q) {
+    const int64_t r = idx / half;
+    const int j = (int)(r % p.Sq), b = (int)(r / p.Sq);
+    p.q_rows[idx] = rope_cs_theta(p.pos_q[b * p.pos_q_sb + j], theta[i], p.rs);
+    return;
+  }
+  idx -= n_q;
+  if (idx < n_k) {
+    const int64_t r = idx / half;
+    const int j = (int)(r % p.Sk), b = (int)(r / p.Sk);
+    p.k_rows[idx] = rope_cs_theta(p.pos_k[b * p.pos_k_sb + j], theta[i], p.rs);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -182,8 +210,6 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
   const int j = idx / q8;
   const int d0 = (idx - j * q8) * 8;
   const bool rot = hk < p.n_rotk;  // uniform over the block
-  // the key position first: its load is then in flight with the row's
-  const int pos = rot ? key_position(p, b, j) : 0;
   const int64_t row = ((int64_t)b * p.n_rot_kv + hk) * p.Sk + j;
   const uint16_t* src = (const uint16_t*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)j * p.ks[2] + d0;
   uint16_t* dst = (uint16_t*)p.k_rot + row * p.D + d0;
@@ -201,15 +227,13 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
     wv0 = *(const u32x4_t*)wp;
     if constexpr (HALF) wv1 = *(const u32x4_t*)(wp + hd);
   }
-  // the pairs' cos / sin from the table row of the position, read as 16-byte
-  // vectors issued before the row is waited for; a position past the table
-  // takes the direct formula at the use (same bits)
+  // the pairs' cos / sin from the key's cos / sin row, read as 16-byte
+  // vectors issued with the K row (no dependent load)
   constexpr int NP = HALF ? 8 : 4;    // pairs of this thread
   const int i0 = HALF ? d0 : d0 / 2;  // first pair index (a multiple of 4)
-  const bool in_tab = pos >= 0 && pos < p.rope_tab_len;
   float4 tv[NP / 2];
   if (rot) {
-    const float4* trow = (const float4*)(p.rope_tab + (size_t)(in_tab ? pos : 0) * (p.D / 2) + i0);
+    const float4* trow = (const float4*)(p.k_cs + ((size_t)b * p.k_cs_sb + j) * (p.D / 2) + i0);
 #pragma unroll
     for (int u = 0; u < NP / 2; ++u) tv[u] = trow[u];
   }
@@ -237,8 +261,7 @@ __global__ __launch_bounds__(256) void k_rotate16_kernel(const FwdParams p) {
       // pair: interleaved (x[2t], x[2t+1]) of pair index d0/2 + t; half
       // split (x[t], x[8+t]) of pair index d0 + t
       const int ia = HALF ? t : 2 * t, ic = HALF ? 8 + t : 2 * t + 1;
-      float2 cs = (t & 1) ? make_float2(tv[t / 2].z, tv[t / 2].w) : make_float2(tv[t / 2].x, tv[t / 2].y);
-      if (__builtin_expect(!in_tab, 0)) cs = rope_cs_direct(pos, i0 + t, p.D, p.rs);
+      const float2 cs = (t & 1) ? make_float2(tv[t / 2].z, tv[t / 2].w) : make_float2(tv[t / 2].x, tv[t / 2].y);
       const float a = x[ia], c = x[ic];
       x[ia] = fmaf(a, cs.x, -c * cs.y);
       x[ic] = fmaf(c, cs.x, a * cs.y);
@@ -279,7 +302,7 @@ __global__ void k_rotate32_kernel(const FwdParams p) {
     x = make_float2(x.x * inv * wp[d0], x.y * inv * wp[d1]);
   }
   if (hk < p.n_rotk) {
-    const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, key_position(p, b, j), i, p.D, p.rs);
+    const float2 cs = p.k_cs[((size_t)b * p.k_cs_sb + j) * half + i];
     x = make_float2(fmaf(x.x, cs.x, -x.y * cs.y), fmaf(x.y, cs.x, x.x * cs.y));
   }
   float* dst = (float*)p.k_rot + row * p.D;
@@ -361,7 +384,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
   {
     const float* qrow = (const float*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi * p.qs[2];
     const bool rot = h < p.n_rot;
-    const int qpos = (rot && qvalid) ? query_position(p, b, qi) : 0;
+    const float2* qcs = p.q_cs + ((size_t)b * p.q_cs_sb + (qvalid ? qi : 0)) * (D / 2);
     // pair i: (2i, 2i+1) interleaved, (i, i + D/2) half split
     const bool half = p.rope_style == 1;
     // RMSNorm of q (one lane holds the whole row)
@@ -377,7 +400,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
       float2 x = qvalid ? make_float2(qrow[d0], qrow[d1]) : make_float2(0.f, 0.f);
       if (wq != nullptr) x = make_float2(x.x * qinv * wq[d0], x.y * qinv * wq[d1]);
       if (rot && qvalid) {
-        const float2 cs = rope_cs(p.rope_tab, p.rope_tab_len, qpos, i, D, p.rs);
+        const float2 cs = qcs[i];
         const float a = fmaf(x.x, cs.x, -x.y * cs.y);
         const float c = fmaf(x.y, cs.x, x.x * cs.y);
         x = make_float2(a, c);
@@ -484,14 +507,16 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const FwdParams p) {
 hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
   const bool f32 = p.dtype == 0;
   const int bm = f32 ? F32_BM : FWD_BM;
-  if (p.n_rot > 0 && p.rope_tab_len > 0) {
-    const int64_t n = (int64_t)p.rope_tab_len * (p.D / 2);
-    rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p.rope_tab, p.rope_tab_len, p.D,
-                                                                              p.rs);
-  }
   if (p.mask_kind == 2) {
     const int nkb = (p.Sk + 255) / 256;
     seg_prep_kernel<<<dim3(p.n_qt > nkb ? p.n_qt : nkb, p.B), dim3(256), 0, s>>>(p, bm);
+  }
+  if (p.n_rot > 0) {
+    // pairs of the table rows, then of the query rows, then of the key rows
+    const int64_t half = p.D / 2;
+    const int64_t n = (int64_t)p.rope_tab_len * half + (p.q_rows ? (int64_t)p.q_rows_b * p.Sq * half : 0) +
+                      (p.k_rows ? (int64_t)p.k_rows_b * p.Sk * half : 0);
+    if (n > 0) rope_prep_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p);
   }
   if (p.mask_kind == 1) {
     // (no key tiles: nothing to classify; the attention kernel visits none)
@@ -502,18 +527,18 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
 }
 
 // Rows of at most KR_MAX_TILES key tiles (16-bit types) rotate their K in
-// the attention kernel: no K pass, one launch per execute.  The rotated
-// keys must then have the default positions 0 .. Sk-1 (inside the cos /
-// sin table, which covers max(Sq, Sk) positions); explicit or
-// segment-derived key positions take the K pass.
+// the attention kernel: no K pass, one launch per execute.  Only with the
+// default key positions 0 .. Sk-1; explicit or segment-derived ones take
+// the K pass (so an explicit position array selects either path for the
+// same keys, which the tests compare bit for bit).
 constexpr int KR_MAX_TILES = 1;
 static bool k_in_attention(const FwdParams& p) {
   if (p.dtype == 0 || p.n_rot_kv == 0 || p.n_kt > KR_MAX_TILES) return false;
-  return p.n_rotk == 0 || (p.pos_k_mode == POS_ARANGE && p.Sk <= p.rope_tab_len);
+  return p.n_rotk == 0 || p.pos_k_mode == POS_ARANGE;
 }
 
-// K heads that get RoPE, rotated into the workspace (reads the table and the
-// derived key positions written by the plan).
+// K heads that get RoPE, rotated into the workspace (reads the keys' cos /
+// sin rows written by the plan).
 hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
   if (p.n_rot_kv > 0 && p.Sk > 0 && p.B > 0 && !k_in_attention(p)) {
     if (p.dtype == 0) {

@@ -10,18 +10,6 @@
 
 namespace mz {
 
-// Positions of keys and queries: 0..S-1, or a user array, or derived from
-// the segment ids by the plan.
-__device__ inline int key_position(const FwdParams& p, int b, int j) {
-  if (p.pos_k_mode == POS_ARANGE) return j;
-  return p.pos_k[b * p.pos_k_sb + j];  // user array, or derived by seg_prep_kernel
-}
-
-__device__ inline int query_position(const FwdParams& p, int b, int i) {
-  if (p.pos_q_mode == POS_ARANGE) return i;
-  return p.pos_q[b * p.pos_q_sb + i];
-}
-
 // ---------------------------------------------------------------------------
 // Main kernel, bf16 / fp16, MFMA 32x32x16.
 //
@@ -138,15 +126,14 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   const bool qvalid = qi < p.Sq;
 
   // ---- Q fragment, pre-scaled: B operand of S^T = K Q^T.  Its loads (q,
-  // the norm weights, the cos / sin table entries) are issued here; the
+  // the norm weights, the query's cos / sin row) are issued here; the
   // arithmetic (finish_q) runs once the first K / V tile copies are
   // issued, so the two latencies overlap.
   // No load here sits inside a per-lane branch (a lane past Sq reads row
   // Sq - 1, and its result is never stored): such a load ends in a wait for
   // everything issued before it, which would make the prologue a chain of
   // round trips.  Loads nobody needs (absent norm weights, waves with no
-  // query) are skipped by wave-uniform branches only.  A position array is
-  // read first, so the table rows that depend on it wait for it alone.
+  // query) are skipped by wave-uniform branches only.
   uint4 qf[NS];
   const int qi_c = qvalid ? qi : p.Sq - 1;
   const uint16_t* qrow = (const uint16_t*)p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qi_c * p.qs[2];
@@ -158,11 +145,6 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // by: every wave-wide load costs the compute unit's load path the same
   // whatever its lanes' addresses.
   const bool wave_live = qt * BM + __builtin_amdgcn_readfirstlane(wave) * 32 < p.Sq;
-  // the query's position: its index, or an array element (a uniform
-  // branch before the other loads, so that the table rows, which need it,
-  // wait for this load alone, and for nothing when there is no array)
-  int qpos = qi_c;
-  if (rot && wave_live && p.pos_q_mode != POS_ARANGE) qpos = p.pos_q[b * p.pos_q_sb + qi_c];
   const float qsc = p.scale_log2;
   // (the one-tile kernels load the q row on every wave: a skipped load's
   // registers merge with the loaded ones, and that merge waits for the
@@ -187,16 +169,15 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
 #pragma unroll
     for (int s = 0; s < NS; ++s) wq[s] = make_uint4(0u, 0u, 0u, 0u);
   }
-  // cos / sin of this lane's pairs at the query's position, read from the
-  // table as 16-byte vectors, all issued before any is used: interleaved,
+  // cos / sin of this lane's pairs, from the query's cos / sin row (the
+  // plan's: no position is read here, so these loads wait for nothing),
+  // read as 16-byte vectors, all issued before any is used: interleaved,
   // piece s holds pairs s*8 + hh*4 + t (t < 4), slot 4s + t; half split,
   // piece s < NS/2 holds pairs s*16 + hh*8 + j (j < 8), slot 8s + j; slot
-  // m is half of tb[m / 2].  A position past the table (rare) takes the
-  // direct formula instead (same bits), a branch at the use.
-  const bool in_tab = qpos >= 0 && qpos < p.rope_tab_len;
+  // m is half of tb[m / 2].
   float4 tb[2 * NS];
   if (rot && wave_live) {
-    const float2* trow = p.rope_tab + (size_t)(in_tab ? qpos : 0) * (D / 2);
+    const float2* trow = p.q_cs + ((size_t)b * p.q_cs_sb + qi_c) * (D / 2);
     if (p.rope_style == 1) {
 #pragma unroll
       for (int s = 0; s < NS / 2; ++s)
@@ -230,19 +211,14 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       const uint32_t w2 = e < 4 ? (e < 2 ? wq[s].x : wq[s].y) : (e < 6 ? wq[s].z : wq[s].w);
       return x * qinv * Elem<T>::to_f32((uint16_t)(w2 >> (16 * (e & 1))));
     };
-    // cos / sin of slot m (pair index pair); DIRECT: a lane whose position
-    // lies past the table takes the direct formula (same bits)
-    auto cs_at = [&](auto direct, int m, int pair) -> float2 {
+    // cos / sin of slot m
+    auto cs_at = [&](int m) -> float2 {
       const float4 v = tb[m >> 1];
-      float2 cs = (m & 1) ? make_float2(v.z, v.w) : make_float2(v.x, v.y);
-      if constexpr (decltype(direct)::value) {
-        if (!in_tab) cs = rope_cs_direct(qpos, pair, D, p.rs);
-      }
-      return cs;
+      return (m & 1) ? make_float2(v.z, v.w) : make_float2(v.x, v.y);
     };
     // half split: element e of chunk s pairs with element e of chunk
     // s + NS/2 (d and d + D/2), both held by this lane
-    auto half_split = [&](auto direct) {
+    auto half_split = [&]() {
 #pragma unroll
       for (int s = 0; s < NS / 2; ++s) {
         uint32_t lo[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
@@ -254,7 +230,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           for (int e = 0; e < 2; ++e) {
             const float a = qn(Elem<T>::to_f32((uint16_t)(lo[t] >> (16 * e))), s, 2 * t + e);
             const float c = qn(Elem<T>::to_f32((uint16_t)(hi[t] >> (16 * e))), s + NS / 2, 2 * t + e);
-            const float2 cs = cs_at(direct, 8 * s + 2 * t + e, s * 16 + hh * 8 + 2 * t + e);
+            const float2 cs = cs_at(8 * s + 2 * t + e);
             r[0][e] = fmaf(a, cs.x, -c * cs.y);
             r[1][e] = fmaf(c, cs.x, a * cs.y);
           }
@@ -266,17 +242,16 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
       }
     };
     // interleaved: the pairs are the two halves of each 32-bit word
-    auto interleaved = [&](auto rotate, auto direct) {
+    auto interleaved = [&](auto rotate) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
-        const int d0 = s * 16 + hh * 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           float a = qn(Elem<T>::to_f32((uint16_t)(wv[t] & 0xFFFF)), s, 2 * t);
           float c = qn(Elem<T>::to_f32((uint16_t)(wv[t] >> 16)), s, 2 * t + 1);
           if constexpr (decltype(rotate)::value) {
-            const float2 cs = cs_at(direct, 4 * s + t, d0 / 2 + t);
+            const float2 cs = cs_at(4 * s + t);
             const float ra = fmaf(a, cs.x, -c * cs.y);
             const float rc = fmaf(c, cs.x, a * cs.y);
             a = ra;
@@ -290,21 +265,11 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     // Every lane of a live wave runs the same code (a lane past Sq holds a
     // copy of row Sq - 1 and its result is never stored), so each branch
     // here is uniform over the wave: no per-lane masking around the
-    // arithmetic.  The direct formula is compiled in only for a wave with a
-    // position past the table.
+    // arithmetic.
     if (!wave_live) return;
-    using yes = std::true_type;
-    using no = std::false_type;
-    const bool direct = !__all(in_tab);
-    if (rot && p.rope_style == 1) {
-      if (direct) half_split(yes{});
-      else half_split(no{});
-    } else if (rot) {
-      if (direct) interleaved(yes{}, yes{});
-      else interleaved(yes{}, no{});
-    } else {
-      interleaved(no{}, no{});
-    }
+    if (rot && p.rope_style == 1) half_split();
+    else if (rot) interleaved(std::true_type{});
+    else interleaved(std::false_type{});
   };
 
   // ---- K / V sources (KR: every head is read from k, through registers)
@@ -663,10 +628,9 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // and written into K stage 0.  Thread piece u is 8 elements of one row
   // (interleaved pairs inside it) or 8 + 8 elements d0 and d0 + D/2 (half
   // split); the pieces of a row are adjacent lanes, so the row's RMSNorm sum
-  // is a shuffle reduction over them.  The keys' positions are their
-  // indices (default positions; the host takes this path only then), all
-  // inside the table.  Every load of the tile (rows, norm weights, the
-  // table rows) is issued right after the Q loads, then the V tile copy, so
+  // is a shuffle reduction over them.  Every load of the tile (rows, norm
+  // weights, the keys' cos / sin rows) is issued right after the Q loads,
+  // then the V tile copy, so
   // the three are in flight together.  Rows past Sk are
   // written as zeros (their keys are masked).  The arithmetic is the K
   // pass's (k_rotate16_kernel).
@@ -683,7 +647,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     float4 tv[NPC * (NP / 2)];
     int jr[NPC];
     // (loads unconditional or under wave-uniform branches only, as in the
-    // Q prologue; the keys' positions are their indices on this path)
+    // Q prologue)
 #pragma unroll
     for (int u = 0; u < NPC; ++u) jr[u] = min(t * BN + (tid + u * 256) / Q8, p.Sk - 1);
     // piece block u covers rows [u * 256 / Q8, (u + 1) * 256 / Q8) of the
@@ -719,8 +683,7 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
           continue;
         }
         const int d0 = ((tid + u * 256) % Q8) * 8;
-        const int pt = jr[u] < p.rope_tab_len ? jr[u] : 0;
-        const float4* trow = (const float4*)(p.rope_tab + (size_t)pt * (D / 2) + (HALF ? d0 : d0 / 2));
+        const float4* trow = (const float4*)(p.k_cs + ((size_t)b * p.k_cs_sb + jr[u]) * (D / 2) + (HALF ? d0 : d0 / 2));
 #pragma unroll
         for (int k = 0; k < NP / 2; ++k) tv[u * (NP / 2) + k] = trow[k];
       }

@@ -52,8 +52,20 @@ struct FwdParams {
   int64_t pos_q_sb;
   const int32_t* pos_k;  // user array (POS_ARRAY) or derived (POS_SEGMENT)
   int64_t pos_k_sb;
-  float2* rope_tab;
+  float2* rope_tab;  // cos / sin of positions [0, rope_tab_len) (plan)
   int rope_tab_len;
+  // cos / sin rows: query i of batch row b rotates with the D/2 pairs at
+  // q_cs + (b * q_cs_sb + i) * D/2, key j with k_cs + (b * k_cs_sb + j) * D/2.
+  // Index positions read the table itself (sb 0); explicit or
+  // segment-derived positions read per-row arrays (q_rows / k_rows, 1 or B
+  // batch rows) that the plan fills from the same formula.
+  const float2* q_cs;
+  int64_t q_cs_sb;
+  const float2* k_cs;
+  int64_t k_cs_sb;
+  float2* q_rows;
+  float2* k_rows;
+  int q_rows_b, k_rows_b;
   void* k_rot;  // [B][n_rot_kv][Sk][D], storage dtype
   // boolean mask
   const uint8_t* mask;
