@@ -426,11 +426,12 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // two so that the arrays swap roles instead of being copied
   f32x16_t sA[2], sB[2];
   float mu = 0.f;  // reference of the exponentials (m, or 0 before any live key)
-  // CINIT (D 64): the K Q^T accumulators start from -mu in every element, so
+  // CINIT: the K Q^T accumulators start from -mu in every element, so
   // scores arrive relative to the reference and the exponentials need no
-  // subtraction.  At D 128 the 16 extra registers would spill; there the
-  // accumulators start from zero and mu is subtracted before each exponential.
-  constexpr bool CINIT = D == 64;
+  // subtraction (32 VALU operations fewer per wave and step).  It costs 16
+  // registers, which fit everywhere but in the two-stream D 128 kernels;
+  // those start from zero and subtract mu before each exponential.
+  constexpr bool CINIT = D == 64 || NSTR == 1;
   f32x16_t cinit = {};
 
   // S^T = K Q^T + cinit of one tile, plain (prologue)
