@@ -181,10 +181,11 @@ int mzattn_fwd(const mzattn_fwd_args* args, void* stream);
  * sampling loop does.
  *
  * mzattn_fwd_plan launches the prepasses that depend on the layout only and
- * writes their results into the workspace: the RoPE cos/sin table (positions
- * 0 .. max position), per-query key ranges and positions derived from the
- * segment ids, and the class of every (query tile, key tile) pair of a
- * boolean mask.  It reads no Q, K or V.
+ * writes their results into the workspace: the RoPE cosines and sines (a
+ * table of the index positions 0 .. seq-1, and one row per query or key
+ * whose position is given or derived from segment ids), per-query key
+ * ranges and positions derived from the segment ids, and the class of every
+ * (query tile, key tile) pair of a boolean mask.  It reads no Q, K or V.
  *
  * mzattn_fwd_execute launches the per-input work: the rotation of the K
  * heads that get RoPE into the workspace, then the attention kernel.  It
