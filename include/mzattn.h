@@ -138,6 +138,11 @@ typedef enum mz_mask_kind {
  *   log-sum-exp of the scaled live scores; -inf for rows with no live key.
  * workspace: device scratch of at least mzattn_fwd_workspace_size() bytes,
  *   256-byte aligned; contents need no initialisation.
+ * key_streams: 0 lets the library choose how the 16-bit kernel walks the
+ *   key tiles of one query tile; 1 forces one chain of steps per query tile,
+ *   2 two chains over alternate tiles merged at the end (a tuning and test
+ *   override: the results agree within rounding).  Other values:
+ *   MZ_ERR_VALUE.  The fp32 kernel ignores it.
  */
 typedef struct mzattn_fwd_args {
   uint32_t struct_size; /* = sizeof(mzattn_fwd_args), else MZ_ERR_ABI */
@@ -170,6 +175,7 @@ typedef struct mzattn_fwd_args {
   float* lse;
   void* workspace;
   size_t workspace_bytes;
+  int32_t key_streams;  /* 0 automatic, 1 or 2 forced */
 } mzattn_fwd_args;
 
 /* Launch the forward on `stream`.  Returns MZ_OK or a negative status.

@@ -114,6 +114,7 @@ class FwdArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("key_streams", ctypes.c_int32),
     ]
 
 
@@ -344,7 +345,8 @@ class FwdCall:
                  scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                  rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
                  rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6,
-                 out=None, return_lse: bool = False, workspace=None, stream=None, _shared_workspace=False):
+                 out=None, return_lse: bool = False, workspace=None, stream=None, key_streams: int = 0,
+                 _shared_workspace=False):
         torch = _torch()
         L = lib()
         B, Hq, Sq, D = q.shape
@@ -371,6 +373,7 @@ class FwdCall:
                 setattr(a, name, w.data_ptr())
                 keep.append(w)
         a.norm_eps = float(norm_eps)
+        a.key_streams = int(key_streams)
         if (mask is not None) + (seg_q is not None) + bool(causal) > 1:
             raise MzattnError(MZ_ERR_UNSUPPORTED, "give at most one of mask, segment ids, causal")
         if causal:
@@ -450,7 +453,8 @@ class FwdCall:
 def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = False, pos_q=None, pos_k=None,
                scale: float = 0.0, rope_base: float = 0.0, pe_attn_head: int = -1,
                rope_style: str = "interleaved", rope_precision: str = "exact", rope_mscale: float = 0.0,
-               rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6, out=None, return_lse: bool = False, workspace=None, stream=None):
+               rope_factors=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6, out=None,
+               return_lse: bool = False, workspace=None, stream=None, key_streams: int = 0):
     """Masked bidirectional attention forward (see ``mzattn_fwd`` in
     include/mzattn.h).  q [B, Hq, Sq, D], k / v [B, Hkv, Sk, D] on one GPU,
     same dtype; mask: bool [B|1, Hq|1, Sq|1, Sk]; seg_q / seg_k: int32
@@ -460,7 +464,8 @@ def mzattn_fwd(q, k, v, *, mask=None, seg_q=None, seg_k=None, causal: bool = Fal
                    scale=scale, rope_base=rope_base, pe_attn_head=pe_attn_head, rope_style=rope_style, rope_precision=rope_precision,
                    rope_mscale=rope_mscale, rope_factors=rope_factors, q_norm_weight=q_norm_weight,
                    k_norm_weight=k_norm_weight, norm_eps=norm_eps, out=out,
-                   return_lse=return_lse, workspace=workspace, stream=stream, _shared_workspace=True)()
+                   return_lse=return_lse, workspace=workspace, stream=stream, key_streams=key_streams,
+                   _shared_workspace=True)()
 
 
 class DecodeCall:

@@ -106,6 +106,8 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
       a->mask_kind != MZ_MASK_CAUSAL)
     return fail(MZ_ERR_UNSUPPORTED, "unknown mask_kind %d", a->mask_kind);
   if (!isfinite(a->scale)) return fail(MZ_ERR_VALUE, "scale is not finite");
+  if (a->key_streams < 0 || a->key_streams > 2)
+    return fail(MZ_ERR_VALUE, "key_streams %d (0 automatic, 1 or 2)", a->key_streams);
   if (!isfinite(a->rope_base) || a->rope_base < 0.0)
     return fail(MZ_ERR_VALUE, "rope_base must be finite and >= 0");
   if (a->rope_base > 0.0 && a->rope_base == 1.0)
@@ -337,6 +339,7 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
   p.Sq = a->seq_q; p.Sk = a->seq_k; p.D = a->head_dim;
   p.n_qt = pl.n_qt; p.n_kt = pl.n_kt;
   p.mask_kind = a->mask_kind;
+  p.key_streams = a->key_streams;
   p.scale_log2 = scale_log2(a->scale, a->head_dim);
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
   for (int i = 0; i < 3; ++i) {

@@ -569,8 +569,8 @@ hipError_t launch_fwd_rotate(const FwdParams& p, hipStream_t s) {
 // With 16 key tiles or fewer per row the second stream's own prologue and
 // the final merge cost more than the shorter chain saves (measured slower
 // at 16 to 1024 keys), and with more work-groups than CUs the one-stream
-// kernel already places two per CU.  MZATTN_KEY_STREAMS=1|2 overrides the
-// choice.
+// kernel already places two per CU.  A caller's key_streams of 1 or 2
+// overrides the choice.
 constexpr int KEY_STREAMS_MIN_TILES = 24;
 // Compute units of the current device, queried once per device.
 static int cu_count() {
@@ -586,11 +586,8 @@ static int cu_count() {
   return n;
 }
 
-static int key_streams(unsigned nwork, int n_kt) {
-  if (const char* e = getenv("MZATTN_KEY_STREAMS")) {
-    if (e[0] == '1' && e[1] == 0) return 1;
-    if (e[0] == '2' && e[1] == 0) return 2;
-  }
+static int key_streams(int forced, unsigned nwork, int n_kt) {
+  if (forced == 1 || forced == 2) return forced;
   if (n_kt < KEY_STREAMS_MIN_TILES) return 1;
   return (int64_t)nwork <= (int64_t)cu_count() ? 2 : 1;
 }
@@ -603,7 +600,7 @@ hipError_t launch_fwd_main(const FwdParams& p, hipStream_t s) {
     else fwd_f32_kernel<128><<<dim3(nwork), dim3(64), 0, s>>>(p);
   } else {
     const bool kr = k_in_attention(p);
-    const int nstr = kr ? 1 : key_streams(nwork, p.n_kt);
+    const int nstr = kr ? 1 : key_streams(p.key_streams, nwork, p.n_kt);
     if (p.dtype == 2) {
       if (p.D == 64) launch_mfma_bf16_d64(p, nwork, nstr, kr, s);
       else launch_mfma_bf16_d128(p, nwork, nstr, kr, s);

@@ -32,6 +32,7 @@ struct FwdParams {
   int dtype, B, Hq, Hkv, G, Sq, Sk, D;
   int n_qt, n_kt;  // query tiles (FWD_BM or F32_BM), key tiles (FWD_BN)
   int mask_kind;
+  int key_streams;   // 0 automatic, 1 or 2 forced (16-bit kernel)
   float scale_log2;  // scale * log2(e)
   const void* q;
   const void* k;

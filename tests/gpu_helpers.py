@@ -19,12 +19,13 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-def run_fwd(case: W.FwdCase, return_lse=False, q=None, k=None, v=None):
+def run_fwd(case: W.FwdCase, return_lse=False, q=None, k=None, v=None, key_streams=0):
     q = dev(case.q) if q is None else q
     k = dev(case.k) if k is None else k
     v = dev(case.v) if v is None else v
     kw = dict(scale=case.scale, rope_base=case.rope_base, pe_attn_head=case.pe_attn_head,
-              rope_style=case.rope_style, pos_q=dev(case.pos_q), pos_k=dev(case.pos_k), return_lse=return_lse)
+              rope_style=case.rope_style, pos_q=dev(case.pos_q), pos_k=dev(case.pos_k), return_lse=return_lse,
+              key_streams=key_streams)
     if case.mask_kind == W.MASK_BOOL:
         kw["mask"] = dev(case.mask)
     elif case.mask_kind == W.MASK_SEGMENT:

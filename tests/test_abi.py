@@ -183,6 +183,8 @@ def fwd_cases():
         ("scale_nan", mutate("scale", float("nan")), B.MZ_ERR_VALUE),
         ("rope_neg", mutate("rope_base", -1.0), B.MZ_ERR_VALUE),
         ("rope_one", mutate("rope_base", 1.0), B.MZ_ERR_VALUE),
+        ("key_streams_3", mutate("key_streams", 3), B.MZ_ERR_VALUE),
+        ("key_streams_neg", mutate("key_streams", -1), B.MZ_ERR_VALUE),
         ("q_null", mutate("q", None), B.MZ_ERR_NULL),
         ("o_null", mutate("o", None), B.MZ_ERR_NULL),
         ("k_null", mutate("k", None), B.MZ_ERR_NULL),

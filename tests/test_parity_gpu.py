@@ -141,15 +141,14 @@ KS_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("streams", ["1", "2"])
+@pytest.mark.parametrize("streams", [1, 2])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", KS_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("kind", ["none", "bool_blocky", "bool_key", "segment"])
-def test_key_streams(monkeypatch, streams, dtype, shape, kind):
+def test_key_streams(streams, dtype, shape, kind):
     """Both work-group shapes of the MFMA kernel (one key stream, or two
     streams over alternate key tiles merged at the end) against the oracle,
     with odd and even live tile counts and tile classes that skip tiles."""
-    monkeypatch.setenv("MZATTN_KEY_STREAMS", streams)
     B, Hq, Hkv, Sq, Sk, D = shape
     seed = zlib.crc32(repr(("ks", dtype, shape, kind)).encode()) % 10000
     if kind == "segment":
@@ -159,7 +158,7 @@ def test_key_streams(monkeypatch, streams, dtype, shape, kind):
     else:
         case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_BOOL,
                             mask_shape={"bool_blocky": "blocky", "bool_key": "key"}[kind], rope_base=1e4)
-    o, lse = run_fwd(case, return_lse=True)
+    o, lse = run_fwd(case, return_lse=True, key_streams=streams)
     ref, lse_ref = oracle_fwd(case)
     assert_parity(dtype, o, ref, f"{case.name} {shape} streams={streams}")
     fin = np.isfinite(lse_ref)
@@ -176,19 +175,18 @@ CAUSAL_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("streams", ["1", "2"])
+@pytest.mark.parametrize("streams", [1, 2])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", CAUSAL_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_causal(monkeypatch, streams, dtype, shape):
+def test_causal(streams, dtype, shape):
     """Causal kind (key j live for query i iff j <= i) against the oracle,
     with RoPE, under both work-group shapes of the MFMA kernel."""
-    monkeypatch.setenv("MZATTN_KEY_STREAMS", streams)
     B, Hq, Hkv, Sq, Sk, D = shape
     if dtype == "f32" and Sq * Sk > 300 * 500:
         pytest.skip("fp32 path: small shapes only")
     seed = zlib.crc32(repr(("causal", dtype, shape)).encode()) % 10000
     case = W.random_fwd(seed, B, Hq, Hkv, Sq, Sk, D, dtype, W.MASK_CAUSAL, rope_base=1e4)
-    o, lse = run_fwd(case, return_lse=True)
+    o, lse = run_fwd(case, return_lse=True, key_streams=streams)
     ref, lse_ref = oracle_fwd(case)
     assert_parity(dtype, o, ref, f"{case.name} {shape} streams={streams}")
     np.testing.assert_allclose(to64(lse), lse_ref, atol=1e-4 if dtype == "f32" else 3e-2)
