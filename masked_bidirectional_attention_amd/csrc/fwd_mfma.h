@@ -327,8 +327,25 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     if constexpr (MK == 1) return cls_in_lds ? cls_lds[kt] : cls_row[kt];
     return 1;
   };
+  // rows of at most 64 key tiles: the live and the mixed tiles as two
+  // wave-uniform bit sets (one class byte per lane, gathered by ballot), so
+  // finding the next live tile and the boundary test are scalar bit
+  // operations with no LDS read in the step
+  const bool cls_bits = MK == 1 && p.n_kt <= 64;
+  uint64_t live_bits = 0, mixed_bits = 0;
+  if constexpr (MK == 1) {
+    if (cls_bits) {
+      const int c = lane < p.n_kt ? (int)cls_row[lane] : 0;
+      live_bits = __ballot(c != 0);
+      mixed_bits = __ballot(c == 2);
+    }
+  }
   auto next_live = [&](int kt) {
     if constexpr (MK == 1) {
+      if (cls_bits) {
+        const uint64_t r = kt < 64 ? live_bits >> kt : 0;
+        return r != 0 ? kt + (int)__builtin_ctzll(r) : kt_end;
+      }
       while (kt < kt_end && cls_at(kt) == 0) ++kt;
     }
     return kt;
@@ -452,7 +469,8 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   auto mask_tile = [&](int kt, f32x16_t (&sc)[2]) {
     bool check;
     if constexpr (MK == 2 || MK == 3) check = !(kt >= full_beg && kt < full_end);
-    else if constexpr (MK == 1) check = cls_at(kt) == 2 || kt >= first_tail_tile;
+    else if constexpr (MK == 1)
+      check = (cls_bits ? ((mixed_bits >> kt) & 1) != 0 : cls_at(kt) == 2) || kt >= first_tail_tile;
     else check = kt >= first_tail_tile;
     if (__builtin_expect(check, 0)) {
       // kept a branch (boundary tiles are few): without the barrier to

@@ -462,6 +462,23 @@ def test_long_segment_rows_fwd(S):
     assert_parity("bf16", o, ref, f"long segments S={S}")
 
 
+@pytest.mark.parametrize("streams", [1, 2])
+@pytest.mark.parametrize("Sk", [4096, 4097, 4200])
+def test_bool_mask_dead_tiles(Sk, streams):
+    """A boolean mask with whole dead 64-key tiles between live and mixed
+    ones, on rows of exactly 64 key tiles (the per-row tile sets fit one
+    64-bit word) and of 65 or 66 (they do not): skipped tiles, boundary tests and
+    the live-tile count of the two-stream split against the oracle."""
+    case = W.random_fwd(77 + Sk, 2, 4, 2, 130, Sk, 64, "bf16", W.MASK_NONE, rope_base=1e4)
+    i = torch.arange(130)[:, None]
+    j = torch.arange(Sk)[None, :]
+    m = (((j // 192) + (i // 100)) % 2 == 0) | ((j % 7 == 0) & (i % 5 == 0))
+    case.mask_kind, case.mask = W.MASK_BOOL, torch.stack([m, ~m])[:, None].contiguous()
+    o = run_fwd(case, key_streams=streams)
+    ref, _ = oracle_fwd(case)
+    assert_parity("bf16", o, ref, f"dead tiles Sk={Sk} streams={streams}")
+
+
 def test_decode_call_set_cache():
     import masked_bidirectional_attention_amd as mz
     a = W.random_decode(32, 2, 8, 2, 1, 500, 128, "bf16", 400, 500)
