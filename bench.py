@@ -329,8 +329,8 @@ def main(argv=None):
         print(json.dumps(counters_from(a.counters_from), indent=1))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     if a.pmc_workload:

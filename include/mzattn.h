@@ -67,7 +67,7 @@ extern "C" {
 #define MZ_ERR_STRIDE (-4)      /* negative stride, or a stride the kernels
                                    cannot take (mask key stride != 1)         */
 #define MZ_ERR_ALIGN (-5)       /* base pointer / stride misaligned           */
-#define MZ_ERR_UNSUPPORTED (-6) /* valid request this build does not cover    */
+#define MZ_ERR_UNSUPPORTED (-6) /* valid request the library does not cover   */
 #define MZ_ERR_WORKSPACE (-7)   /* workspace missing, too small or misaligned */
 #define MZ_ERR_ABI (-8)         /* struct_size does not match this library    */
 #define MZ_ERR_HIP (-9)         /* a HIP launch failed                        */

@@ -38,7 +38,7 @@ to follow step by step):
     o_i  = sum_j p_ij v_j / l_i,  lse_i = m_i + ln l_i
     no live key: o_i = 0, lse_i = -inf
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 True in a mask means "takes part"; a query with no live key gives 0;
 interleaved RoPE rotates adjacent pairs (2i, 2i+1) by pos * base^(-2i/D);
 with GQA, query head h reads K/V head floor(h / G); causal follows SDPA's
@@ -178,8 +178,8 @@ def rope_half_split(x: np.ndarray, pos: np.ndarray, base: float, precision: str 
                     mscale: float = 1.0) -> np.ndarray:
     """Rotate the pairs (x_i, x_i+D/2) of every row of x [..., S, D] by the
     angle pos * theta_i: the "rotate half" pairing of GPT-NeoX / Llama-style
-    models, offered beside the interleaved one (the pages' other models; the
-    survey's RoPE-variants item).  Same frequencies and rotation sense."""
+    models, offered beside the interleaved one for the pages' other models.
+    Same frequencies and rotation sense."""
     D = x.shape[-1]
     c, s = rope_cos_sin(pos, D, base, precision, factors, mscale)
     x0, x1 = x[..., :D // 2], x[..., D // 2:]

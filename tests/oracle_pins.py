@@ -623,7 +623,7 @@ def pin_qk_rms_norm():
 
 
 # --------------------------------------------------------------------------
-# the comparison that decides every GPU parity verdict
+# the comparison that decides every GPU parity check
 # --------------------------------------------------------------------------
 
 
@@ -667,7 +667,7 @@ def pin_parity_checker():
             st = mzref.parity_stats(out, big)
             assert st["rel_l2"] < 1e-3 and st["max_ref"] == 2.0
             assert ok(dt, out, big) is want, f"{dt} max-abs {frac}"
-        # the same bump on an ordinary element is judged against max |ref|
+        # the same bump on an ordinary element is measured against max |ref|
         out = big.copy()
         out[9] += 0.0202 * 2.0
         assert not ok(dt, out, big), f"{dt} max-abs on a non-maximal element"
