@@ -479,6 +479,43 @@ def test_bool_mask_dead_tiles(Sk, streams):
     assert_parity("bf16", o, ref, f"dead tiles Sk={Sk} streams={streams}")
 
 
+@pytest.mark.parametrize("kind", ["none", "bool_key"])
+def test_max_key_length_fwd(kind):
+    """The longest key row the forward accepts (2^20 keys: 16384 key tiles,
+    class bytes read from global memory, two key streams over one query
+    tile) against the oracle."""
+    Sk = 1 << 20
+    if kind == "none":
+        case = W.random_fwd(91, 1, 2, 1, 40, Sk, 64, "bf16", W.MASK_NONE, rope_base=1e4)
+    else:
+        case = W.random_fwd(92, 1, 2, 1, 40, Sk, 64, "bf16", W.MASK_BOOL, mask_shape="key", rope_base=1e4)
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity("bf16", o, ref, f"max key length {kind}")
+
+
+def test_decode_max_cache():
+    """The largest static cache the decode accepts (2^24 positions, 131072
+    chunks, 2048 merge super-groups): 1000 live keys, the rest finite junk
+    under the mask.  Full span and the span cut after the live keys give the
+    same bits, and both match the oracle on the live part."""
+    import masked_bidirectional_attention_amd as mz
+    C, small = 1 << 24, 1024
+    case = W.random_decode(93, 1, 2, 1, 1, small, 64, "bf16", filled=1000, span=small)
+    kb = torch.full((1, 1, C, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    vb = torch.full((1, 1, C, 64), -5.0, dtype=torch.bfloat16, device=DEV)
+    kb[:, :, :small] = dev(case.k_cache)
+    vb[:, :, :small] = dev(case.v_cache)
+    mb = torch.zeros((1, 1, 1, C), dtype=torch.bool, device=DEV)
+    mb[..., :small] = dev(case.mask)
+    outs = []
+    for span in (C, small):
+        outs.append(mz.mzattn_decode(dev(case.q), kb, vb, span=span, mask=mb, scale=case.scale))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "span truncation changed bits"
+    assert_parity("bf16", outs[0], oracle_decode(case), "max cache")
+
+
 def test_decode_call_set_cache():
     import masked_bidirectional_attention_amd as mz
     a = W.random_decode(32, 2, 8, 2, 1, 500, 128, "bf16", 400, 500)
