@@ -494,6 +494,23 @@ def test_max_key_length_fwd(kind):
     assert_parity("bf16", o, ref, f"max key length {kind}")
 
 
+@pytest.mark.parametrize("shape,dtype,kind", [
+    ((65535, 1, 1, 3, 5, 64), "bf16", "bool_key"),   # largest batch, K rotated in the attention kernel
+    ((65535, 1, 1, 3, 5, 64), "f32", "bool_key"),
+    ((1, 65535, 1, 3, 70, 64), "bf16", "none"),      # largest head count, one kv-head (G = 65535), K pass
+], ids=["batch-bf16", "batch-f32", "heads-bf16"])
+def test_max_batch_and_heads(shape, dtype, kind):
+    """The largest batch and head counts the forward accepts (65535 each)
+    against the oracle: grids of 65535 work-groups and K-pass grids with
+    65535 batch rows."""
+    B, Hq, Hkv, Sq, Sk, D = shape
+    mk = W.MASK_BOOL if kind == "bool_key" else W.MASK_NONE
+    case = W.random_fwd(94, B, Hq, Hkv, Sq, Sk, D, dtype, mk, mask_shape="key", rope_base=1e4)
+    o = run_fwd(case)
+    ref, _ = oracle_fwd(case)
+    assert_parity(dtype, o, ref, f"max batch / heads {shape} {dtype}")
+
+
 def test_decode_max_cache():
     """The largest static cache the decode accepts (2^24 positions, 131072
     chunks, 2048 merge super-groups): 1000 live keys, the rest finite junk
