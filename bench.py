@@ -344,6 +344,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    info = mz.mzattn_device_info(0)
 
     # ---- inputs resident in HBM
     c3 = W.qwen_cfg_packed()
@@ -357,7 +358,8 @@ def main(argv=None):
     copies = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(max(0, a.cache_copies - 1))]
     dec = mz.DecodeCall(dq, kc0, vc0, span=8192, mask=dmask, scale=c4.scale)
     torch.cuda.synchronize()
-    print(f"[bench] device {props.name}, {props.multi_processor_count} CUs; inputs resident", file=sys.stderr, flush=True)
+    print(f"[bench] device {props.name} {info['arch']}, {info['compute_units']} CUs, peak engine clock "
+          f"{info['clock_mhz']:.0f} MHz; inputs resident", file=sys.stderr, flush=True)
 
     # the layout prepasses, once (they depend on the segment ids alone)
     fwd.plan()
@@ -781,7 +783,8 @@ def main(argv=None):
         "decode_append": {"workload": "append step: B 2, 1 new token, Hq 16 / Hkv 2, D 128, bf16, cache 8192, "
                                       "length on the device, RoPE base 1e4 on q and the new key",
                           "by_fill": append},
-        "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)",
+        "device": {"name": props.name, "arch": info["arch"], "compute_units": info["compute_units"],
+                   "peak_engine_clock_mhz": info["clock_mhz"], "memory_clock_mhz": info["mem_clock_mhz"]},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host ...", file=sys.stderr, flush=True)

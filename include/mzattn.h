@@ -366,6 +366,12 @@ const char* mzattn_strerror(int status);
 const char* mzattn_last_error(void);
 /* MZATTN_VERSION of the built library. */
 int mzattn_version(void);
+/* What the HIP runtime reports for `device`, for labelling measurements:
+ * compute units, peak engine and memory clocks in kHz, and the gfx target
+ * name (with its feature flags) copied into `arch` (at most arch_len bytes,
+ * NUL-terminated).  Any output pointer may be NULL.  Returns MZ_OK, or
+ * MZ_ERR_HIP when the runtime query fails (no such device). */
+int mzattn_device_info(int device, int* compute_units, int* clock_khz, int* mem_clock_khz, char* arch, int arch_len);
 
 #ifdef __cplusplus
 } /* extern "C" */

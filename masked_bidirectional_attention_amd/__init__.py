@@ -16,7 +16,8 @@ from ._binding import (  # noqa: F401
     mzattn_decode,
     mzattn_decode_append,
     mzattn_decode_noalloc,
+    mzattn_device_info,
     mzattn_fwd,
 )
 
-__all__ = ["DecodeCall", "DecodeAppendCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "mzattn_decode_append", "mzattn_decode_noalloc", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]
+__all__ = ["DecodeCall", "DecodeAppendCall", "FwdCall", "mzattn_fwd", "mzattn_decode", "mzattn_decode_append", "mzattn_decode_noalloc", "mzattn_device_info", "MzattnError", "MzattnNotBuilt", "lib", "LIB_PATH"]

@@ -210,6 +210,8 @@ _SIGNATURES = {
     "mzattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mzattn_last_error": (ctypes.c_char_p, []),
     "mzattn_version": (ctypes.c_int, []),
+    "mzattn_device_info": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_int), ctypes.c_char_p, ctypes.c_int]),
 }
 
 _lib = None
@@ -628,3 +630,15 @@ def mzattn_decode_append(q, k_new, v_new, k_cache, v_cache, length, *, mask=None
                             rope_base=rope_base, rope_style=rope_style, rope_precision=rope_precision,
                             rope_mscale=rope_mscale, rope_factors=rope_factors, overflow=overflow, out=out,
                             workspace=workspace, stream=stream)()
+
+
+def mzattn_device_info(device: int = 0) -> dict:
+    """What the HIP runtime reports for ``device`` (``mzattn_device_info``
+    in include/mzattn.h): compute units, peak engine and memory clocks in
+    MHz, and the gfx target name."""
+    L = lib()
+    cu, clk, mclk = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    arch = ctypes.create_string_buffer(64)
+    _check(L.mzattn_device_info(int(device), ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(mclk), arch, 64))
+    return {"compute_units": cu.value, "clock_mhz": clk.value / 1000.0, "mem_clock_mhz": mclk.value / 1000.0,
+            "arch": arch.value.decode()}

@@ -429,6 +429,24 @@ extern "C" {
 
 int mzattn_version(void) { return MZATTN_VERSION; }
 
+int mzattn_device_info(int device, int* compute_units, int* clock_khz, int* mem_clock_khz, char* arch, int arch_len) {
+  hipDeviceProp_t prop;
+  const hipError_t e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) {
+    // the failed query leaves its error as the thread's last HIP error;
+    // take it back so that the next launch check does not report it
+    (void)hipGetLastError();
+    return fail(MZ_ERR_HIP, "hipGetDeviceProperties(%d): %s", device, hipGetErrorString(e));
+  }
+  if (compute_units) *compute_units = prop.multiProcessorCount;
+  if (clock_khz) *clock_khz = prop.clockRate;
+  if (mem_clock_khz) *mem_clock_khz = prop.memoryClockRate;
+  if (arch != nullptr && arch_len > 0) {
+    snprintf(arch, (size_t)arch_len, "%s", prop.gcnArchName);
+  }
+  return MZ_OK;
+}
+
 const char* mzattn_strerror(int status) {
   switch (status) {
     case MZ_OK: return "ok";

@@ -147,6 +147,14 @@ int main() {
   f.struct_size = 1;
   bad |= check_status(mzattn_validate_fwd(&f));
   for (int s = -20; s <= 5; ++s) (void)mzattn_strerror(s);
+  {
+    // with no device the query fails cleanly, whatever the outputs
+    char arch[4];
+    int cu = -1;
+    bad |= check_status(mzattn_device_info(0, &cu, nullptr, nullptr, arch, (int)sizeof(arch)));
+    bad |= check_status(mzattn_device_info(-1, nullptr, nullptr, nullptr, nullptr, 0));
+    if (mzattn_device_info(0, &cu, nullptr, nullptr, arch, (int)sizeof(arch)) != MZ_ERR_HIP || cu != -1) bad = 1;
+  }
   printf("%d calls checked, version %d\n", checked, mzattn_version());
   return bad;
 }

@@ -1,7 +1,8 @@
 // The handful of HIP runtime calls the C-ABI host code makes, for a build
 // that runs without a GPU: code-object registration does nothing, the
-// device is 0, and the address of the library's device array is a host
-// buffer of the same size (only ever passed on to the stub launchers).
+// device is 0, the address of the library's device array is a host buffer
+// of the same size (only ever passed on to the stub launchers), and the
+// device property query reports that there is no device.
 #include <stddef.h>
 
 namespace {
@@ -22,4 +23,7 @@ int hipGetSymbolAddress(void** ptr, const void*) {
   return 0;
 }
 const char* hipGetErrorString(int) { return "stub runtime error"; }
+// no device to describe: the property query fails (hipErrorNoDevice)
+int hipGetDevicePropertiesR0600(void*, int) { return 100; }
+int hipGetLastError(void) { return 0; }
 }

@@ -1008,3 +1008,18 @@ def test_query_positions_past_the_table(dtype, style, shape):
     ref, _ = mzref.mzref_fwd(dtype, W.to_bits(case.q), W.to_bits(case.k), W.to_bits(case.v), rope_base=1e4,
                              rope_style=style, pos_q=pos_q, pos_k=np.arange(Sk, dtype=np.int32)[None].repeat(B, 0))
     assert_parity(dtype, o, ref, f"positions past the table {style} {shape}")
+
+
+def test_device_info():
+    """The device query names the part the measurements run on."""
+    import masked_bidirectional_attention_amd as mz
+    info = mz.mzattn_device_info(0)
+    props = torch.cuda.get_device_properties(0)
+    assert info["compute_units"] == props.multi_processor_count > 0
+    assert info["arch"].split(":")[0] == props.gcnArchName.split(":")[0]
+    assert info["clock_mhz"] > 0 and info["mem_clock_mhz"] > 0
+    with pytest.raises(mz.MzattnError):
+        mz.mzattn_device_info(torch.cuda.device_count())
+    # the failed query leaves no HIP error behind for the next launch
+    case = W.random_fwd(95, 1, 2, 1, 20, 30, 64, "bf16", rope_base=1e4)
+    assert_parity("bf16", run_fwd(case), oracle_fwd(case)[0], "launch after a failed device query")
