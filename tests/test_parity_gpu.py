@@ -343,6 +343,33 @@ def test_deterministic():
     assert torch.equal(run_decode(d), run_decode(d))
 
 
+def test_calls_on_two_streams_at_once():
+    """Forward and decode calls issued on two streams with nothing ordering
+    them (each call with its own workspace: the one-shot entry points keep
+    one per stream) give the bits of the same calls made one at a time."""
+    import masked_bidirectional_attention_amd as mz
+    fa = W.random_fwd(96, 2, 8, 2, 333, 333, 128, "bf16", W.MASK_SEGMENT, rope_base=1e6, n_segments=3)
+    fb = W.random_fwd(97, 2, 16, 16, 300, 300, 64, "f16", W.MASK_BOOL, mask_shape="blocky", rope_base=1e4)
+    dc = W.vox_decode(3100)
+    ref = [run_fwd(fa), run_fwd(fb), run_decode(dc)]
+    ins = [[dev(x) for x in (c.q, c.k, c.v)] for c in (fa, fb)]
+    seg, mask = dev(fa.seg_q), dev(fb.mask)
+    dq, dk, dv, dm = dev(dc.q), dev(dc.k_cache), dev(dc.v_cache), dev(dc.mask)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa = mz.mzattn_fwd(*ins[0], seg_q=seg, seg_k=seg, rope_base=1e6, stream=s1)
+            od = mz.mzattn_decode(dq, dk, dv, span=dc.span, mask=dm, scale=dc.scale, stream=s1)
+        with torch.cuda.stream(s2):
+            ob = mz.mzattn_fwd(*ins[1], mask=mask, rope_base=1e4, stream=s2)
+        outs.append((oa, ob, od))
+    torch.cuda.synchronize()
+    for oa, ob, od in outs:
+        assert torch.equal(oa, ref[0]) and torch.equal(ob, ref[1]) and torch.equal(od, ref[2])
+
+
 def test_gqa_equals_repeated_heads():
     case = W.random_fwd(28, 1, 8, 2, 200, 200, 128, "bf16", W.MASK_BOOL, mask_shape="bcast_h", rope_base=1e6)
     a = run_fwd(case)
