@@ -177,18 +177,15 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // m is half of tb[m / 2].
   float4 tb[2 * NS];
   if (rot && wave_live) {
-    const float2* trow = p.q_cs + ((size_t)b * p.q_cs_sb + qi_c) * (D / 2);
-    if (p.rope_style == 1) {
-#pragma unroll
-      for (int s = 0; s < NS / 2; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tb[4 * s + j] = ((const float4*)(trow + s * 16 + hh * 8))[j];
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) tb[2 * s + j] = ((const float4*)(trow + s * 8 + hh * 4))[j];
-    }
+    // the style only picks each slot's offset (a uniform select between two
+    // constants), so either pairing costs the same 2 * NS 16-byte loads
+    const bool hs = p.rope_style == 1;
+    const float2* tl = p.q_cs + ((size_t)b * p.q_cs_sb + qi_c) * (D / 2) + hh * (hs ? 8 : 4);
+    static_for<2 * NS>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int oi = (m >> 1) * 8 + (m & 1) * 2, oh = (m >> 2) * 16 + (m & 3) * 2;
+      tb[m] = *(const float4*)(tl + (hs ? oh : oi));
+    });
   }
   auto finish_q = [&]() {
     float qinv = 1.f;
