@@ -662,6 +662,11 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     u32x4_t a0[NPC], a1[NPC], w0[NPC], w1[NPC];
     float4 tv[NPC * (NP / 2)];
     int jr[NPC];
+    // The V tile's copies go first: the waits for the K rows below are
+    // waits for everything issued before them (the copies are invisible to
+    // the compiler's counters), so copies issued after the K loads would
+    // hold the rotation until the V tile had landed too.
+    load_v(t, 0);
     // (loads unconditional or under wave-uniform branches only, as in the
     // Q prologue)
 #pragma unroll
@@ -704,7 +709,6 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
         for (int k = 0; k < NP / 2; ++k) tv[u * (NP / 2) + k] = trow[k];
       }
     }
-    load_v(t, 0);
     uint16_t* kst = &Ks[0][0][0];
 #pragma unroll
     for (int u = 0; u < NPC; ++u) {
