@@ -662,10 +662,11 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
     u32x4_t a0[NPC], a1[NPC], w0[NPC], w1[NPC];
     float4 tv[NPC * (NP / 2)];
     int jr[NPC];
-    // The V tile's copies go first: the waits for the K rows below are
-    // waits for everything issued before them (the copies are invisible to
-    // the compiler's counters), so copies issued after the K loads would
-    // hold the rotation until the V tile had landed too.
+    // The V tile's copies go first.  The compiler waits for the K rows
+    // below by counting only the loads it can see (the copies are opaque to
+    // it), so copies issued after the K loads would be waited for too;
+    // issued before them they land first (vector memory completes in
+    // order), and the wait for the K rows costs nothing more.
     load_v(t, 0);
     // (loads unconditional or under wave-uniform branches only, as in the
     // Q prologue)
