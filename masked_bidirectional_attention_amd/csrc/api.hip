@@ -67,8 +67,9 @@ struct FwdPlan {
   int n_rot = 0, n_rot_kv = 0, n_rotk = 0, tab_len = 0;
   int Bm = 1, Hm = 1;
   size_t off_tab = 0, off_krot = 0, off_qrange = 0, off_qtrange = 0, off_qpos = 0, off_kpos = 0, off_cls = 0;
-  size_t off_bits = 0, off_qrows = 0, off_krows = 0;
+  size_t off_bits = 0, off_qrows = 0, off_krows = 0, off_qcst = 0;
   int q_rows_b = 0, k_rows_b = 0;  // batch rows of the cos / sin row arrays (0: none)
+  int q_cst_b = 0;                 // batch rows of the chunk-major query cos / sin (0: none)
   int mask_rows = 0;
   bool need_qpos = false;
   size_t bytes = 0;
@@ -176,6 +177,10 @@ int plan_fwd(const mzattn_fwd_args* a, FwdPlan* pl) {
     if (k_rows) {
       pl->k_rows_b = (a->pos_k != nullptr && a->pos_k_stride_b == 0) ? 1 : a->batch;
       pl->off_krows = carve((size_t)pl->k_rows_b * a->seq_k * (D / 2) * sizeof(float) * 2);
+    }
+    if (a->dtype != MZ_F32 && a->seq_q > 0) {
+      pl->q_cst_b = q_rows ? pl->q_rows_b : 1;
+      pl->off_qcst = carve((size_t)pl->q_cst_b * a->seq_q * (D / 2) * sizeof(float) * 2);
     }
   }
   if (pl->n_rot_kv > 0) pl->off_krot = carve((size_t)a->batch * pl->n_rot_kv * a->seq_k * D * elem_size(a->dtype));
@@ -361,6 +366,11 @@ void fill_fwd_params(const mzattn_fwd_args* a, const FwdPlan& pl, mz::FwdParams&
       p.q_cs_sb = pl.q_rows_b == 1 ? 0 : a->seq_q;
     } else {
       p.q_cs = p.rope_tab;
+    }
+    if (pl.q_cst_b > 0) {
+      p.q_cst = reinterpret_cast<float4*>(ws + pl.off_qcst);
+      p.q_cst_b = pl.q_cst_b;
+      p.q_cst_sb = pl.q_cst_b == 1 ? 0 : (int64_t)(a->head_dim / 4) * a->seq_q;
     }
     if (pl.k_rows_b > 0) {
       p.k_rows = reinterpret_cast<float2*>(ws + pl.off_krows);

@@ -23,7 +23,10 @@ namespace mz {
 //   the query rows, row b * Sq + i = position pos_q[b * pos_q_sb + i], for
 //   q_rows_b batch rows, when the positions are given or derived from
 //   segments;
-//   the key rows likewise.
+//   the key rows likewise;
+//   for the 16-bit kernels, the query rows again in chunk-major order (the
+//   16-byte chunk c of every query of a batch row, then chunk c + 1), so
+//   that the 32 queries of a wave read contiguous bytes in the Q prologue.
 // The kernels after the plan read these rows and need neither the
 // positions nor the direct formula.  In segment mode it runs after the
 // segment prepass, which derives the positions.
@@ -37,6 +40,7 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const FwdParams p) {
   const int64_t n_tab = (int64_t)p.rope_tab_len * half;
   const int64_t n_q = p.q_rows != nullptr ? (int64_t)p.q_rows_b * p.Sq * half : 0;
   const int64_t n_k = p.k_rows != nullptr ? (int64_t)p.k_rows_b * p.Sk * half : 0;
+  const int64_t n_c = p.q_cst != nullptr ? (int64_t)p.q_cst_b * p.Sq * half : 0;
   const int i = (int)(idx % half);
   if (idx < n_tab) {
     p.rope_tab[idx] = rope_cs_theta((int)(idx / half), theta[i], p.rs);
@@ -54,6 +58,19 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const FwdParams p) {
     const int64_t r = idx / half;
     const int j = (int)(r % p.Sk), b = (int)(r / p.Sk);
     p.k_rows[idx] = rope_cs_theta(p.pos_k[b * p.pos_k_sb + j], theta[i], p.rs);
+    return;
+  }
+  idx -= n_k;
+  if (idx < n_c) {
+    // chunk-major query rows: element idx is pair 2c + e of query j, batch
+    // row b, at ((b * D/4 + c) * Sq + j) * 2 + e
+    const int e = (int)(idx & 1);
+    const int64_t r = idx >> 1;
+    const int j = (int)(r % p.Sq);
+    const int64_t r2 = r / p.Sq;
+    const int c = (int)(r2 % (half / 2)), b = (int)(r2 / (half / 2));
+    const int pos = p.pos_q_mode == POS_ARANGE ? j : p.pos_q[b * p.pos_q_sb + j];
+    reinterpret_cast<float2*>(p.q_cst)[idx] = rope_cs_theta(pos, theta[2 * c + e], p.rs);
   }
 }
 
@@ -515,7 +532,8 @@ hipError_t launch_fwd_plan(const FwdParams& p, hipStream_t s) {
     // pairs of the table rows, then of the query rows, then of the key rows
     const int64_t half = p.D / 2;
     const int64_t n = (int64_t)p.rope_tab_len * half + (p.q_rows ? (int64_t)p.q_rows_b * p.Sq * half : 0) +
-                      (p.k_rows ? (int64_t)p.k_rows_b * p.Sk * half : 0);
+                      (p.k_rows ? (int64_t)p.k_rows_b * p.Sk * half : 0) +
+                      (p.q_cst ? (int64_t)p.q_cst_b * p.Sq * half : 0);
     if (n > 0) rope_prep_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p);
   }
   if (p.mask_kind == 1) {

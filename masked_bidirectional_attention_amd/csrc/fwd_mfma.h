@@ -179,12 +179,15 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   if (rot && wave_live) {
     // the style only picks each slot's offset (a uniform select between two
     // constants), so either pairing costs the same 2 * NS 16-byte loads
+    // slot m is chunk (hs ? oh : oi) + hh * (hs ? 4 : 2) of the query's
+    // row (float4 chunk c = pairs 2c, 2c + 1), read from the plan's
+    // chunk-major copy: the 32 queries of a wave are contiguous per load
     const bool hs = p.rope_style == 1;
-    const float2* tl = p.q_cs + ((size_t)b * p.q_cs_sb + qi_c) * (D / 2) + hh * (hs ? 8 : 4);
+    const float4* tl = p.q_cst + b * p.q_cst_sb + (int64_t)(hh * (hs ? 4 : 2)) * p.Sq + qi_c;
     static_for<2 * NS>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int oi = (m >> 1) * 8 + (m & 1) * 2, oh = (m >> 2) * 16 + (m & 3) * 2;
-      tb[m] = *(const float4*)(tl + (hs ? oh : oi));
+      constexpr int oi = (m >> 1) * 4 + (m & 1), oh = (m >> 2) * 8 + (m & 3);
+      tb[m] = tl[(int64_t)(hs ? oh : oi) * p.Sq];
     });
   }
   auto finish_q = [&]() {

@@ -67,6 +67,13 @@ struct FwdParams {
   float2* q_rows;
   float2* k_rows;
   int q_rows_b, k_rows_b;
+  // the queries' cos / sin again, chunk-major for the 16-bit kernels' Q
+  // prologue: float4 (pairs 2c, 2c + 1) of query i at q_cst + b * q_cst_sb
+  // + c * Sq + i, c < D / 4 (q_cst_b batch rows, sb 0 when shared), so the
+  // 32 queries of a wave read 512 contiguous bytes per load
+  float4* q_cst;
+  int64_t q_cst_sb;
+  int q_cst_b;
   void* k_rot;  // [B][n_rot_kv][Sk][D], storage dtype
   // boolean mask
   const uint8_t* mask;
