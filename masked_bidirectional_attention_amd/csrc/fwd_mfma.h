@@ -920,6 +920,42 @@ __global__ __launch_bounds__(256 * NSTR, 3 - NSTR) void fwd_mfma_kernel(const Fw
   // ---- epilogue: O = O^T / l, lse
   const float l_tot = half_swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // One key stream, all 32 rows of the wave inside Sq (a wave-uniform
+  // test): the wave stages its output rows in its own quarter of the K
+  // stages (no K stage is read after the last step's barrier) and stores
+  // whole rows, 1 KB per instruction, where the MFMA layout would store 16
+  // bytes of each of 32 rows per instruction.  (A partly filled wave, as in
+  // rows of a few tokens, keeps the direct stores: there the staging's LDS
+  // round trip measured slower than the scattered stores it saves.)
+  if (NSTR == 1 && qt * BM + __builtin_amdgcn_readfirstlane(wave) * 32 + 32 <= p.Sq) {
+    constexpr int OS = KS;                     // padded row, elements
+    constexpr int NCH = D / 8;                 // 16-byte chunks per row
+    static_assert(4 * 32 * OS <= 2 * BN * KS, "four waves' rows fit the K stages");
+    uint16_t* ost = &Ks[0][0][0] + wave * 32 * OS;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 st;
+        st.x = Elem<T>::pack2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
+        st.y = Elem<T>::pack2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
+        *(uint2*)&ost[l32 * OS + db * 32 + g4 * 8 + hh * 4] = st;
+      }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    const int q0 = qt * BM + wave * 32;
+    uint16_t* obase = (uint16_t*)p.o + b * p.os[0] + h * p.os[1];
+#pragma unroll
+    for (int it = 0; it < 32 * NCH / 64; ++it) {
+      const int q = it * 64 + lane, r = q / NCH, c = q % NCH;
+      const uint4 v = *(const uint4*)&ost[r * OS + c * 8];
+      if (q0 + r < p.Sq) *(uint4*)(obase + (int64_t)(q0 + r) * p.os[2] + c * 8) = v;
+    }
+    if (qvalid && p.lse != nullptr && hh == 0)
+      p.lse[((int64_t)b * p.Hq + h) * p.Sq + qi] =
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    return;
+  }
   if (qvalid) {
     uint16_t* orow = (uint16_t*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)qi * p.os[2];
 #pragma unroll
